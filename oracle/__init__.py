@@ -1,0 +1,6 @@
+"""CPU oracle (test infrastructure only; see moe_oracle's header)."""
+from .moe_oracle import (activation, combine, expert_ffn, gather_rows, gelu, moe_layer,
+                         permute, route_topk, silu)
+
+__all__ = ["activation", "combine", "expert_ffn", "gather_rows", "gelu", "moe_layer",
+           "permute", "route_topk", "silu"]

@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle: each check compares it with something other than itself.
+
+The pages print no worked example, so the oracle is pinned by brute force on
+tiny inputs, closed forms, independent library routines (torch fp64 GELU/SiLU,
+numpy argmax, scipy softmax), a hand-derived permutation example, and
+invariants that the definitions in "Comet: Fine-grained Computation-
+communication Overlapping for Mixture-of-Experts" section 2.1 imply (top-k
+reduce, expert parallelism) and section 3.1.2 (source-rank sort, tile-aligned
+regrouping, local tiles first).
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import moe_oracle as O
+
+
+# ---------------------------------------------------------------------------
+# helpers (independent formulations)
+# ---------------------------------------------------------------------------
+
+def brute_topk(row, k):
+    """Max exact-sum k-subset; ties -> lexicographically smallest ascending id tuple.
+    Slot order: selected ids by (logit desc, id asc)."""
+    E = len(row)
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(E), k):   # ascending tuples, lexicographic order
+        s = sum(Fraction(float(row[e])) for e in sub)
+        if best_sum is None or s > best_sum:
+            best, best_sum = sub, s
+    return sorted(best, key=lambda e: (-float(row[e]), e))
+
+
+def rand_weights(rng, E, H, F, act, scale=0.3):
+    ws = []
+    for _ in range(E):
+        w0 = rng.standard_normal((F, H)) * scale
+        w0u = rng.standard_normal((F, H)) * scale if act == "swiglu" else None
+        w1 = rng.standard_normal((H, F)) * scale
+        ws.append((w0, w0u, w1))
+    return ws
+
+
+def torch_ffn(X, w, act):
+    """Dense FFN of all rows of X with torch fp64 library ops (independent of the oracle)."""
+    w0, w0u, w1 = w
+    Xt = torch.tensor(X, dtype=torch.float64)
+    g = Xt @ torch.tensor(w0, dtype=torch.float64).T
+    if act == "swiglu":
+        u = Xt @ torch.tensor(w0u, dtype=torch.float64).T
+        a = torch.nn.functional.silu(g) * u
+    else:
+        a = torch.nn.functional.gelu(g, approximate="none")
+    return (a @ torch.tensor(w1, dtype=torch.float64).T).numpy()
+
+
+def dense_mixture(X, L, k, ws, act, expert_begin=0, E_loc=None, renormalize=True):
+    """Every expert on every token, mixed by a dense [T, E] gate with zeros off the top-k."""
+    T, E = L.shape
+    E_loc = E if E_loc is None else E_loc
+    G = np.zeros((T, E))
+    for t in range(T):
+        sel = brute_topk(L[t], k)
+        if renormalize:
+            G[t, sel] = scipy.special.softmax(L[t, sel].astype(np.float64))
+        else:
+            G[t, sel] = scipy.special.softmax(L[t].astype(np.float64))[sel]
+    out = np.zeros((T, X.shape[1]))
+    for le in range(E_loc):
+        out += G[:, expert_begin + le, None] * torch_ffn(X, ws[le], act)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def test_topk1_is_argmax_with_ties():
+    rng = np.random.default_rng(0)
+    L = rng.integers(-3, 4, size=(200, 7)).astype(np.float32)   # many ties
+    idx, w = O.route_topk(L, 1)
+    assert np.array_equal(idx[:, 0], np.argmax(L, axis=1))     # argmax returns the lowest index on ties
+    assert np.all(w == 1.0)
+
+
+@pytest.mark.parametrize("E", [2, 3, 5, 6])
+def test_topk_matches_bruteforce(E):
+    rng = np.random.default_rng(E)
+    for k in range(1, E + 1):
+        L = rng.integers(-2, 3, size=(40, E)).astype(np.float32)
+        L[::3] = rng.standard_normal((len(L[::3]), E)).astype(np.float32)  # mix tied and distinct rows
+        idx, _ = O.route_topk(L, k)
+        for t in range(len(L)):
+            assert list(idx[t]) == brute_topk(L[t], k), (E, k, t, L[t])
+
+
+def test_gate_weights_sum_to_one_and_ratios():
+    rng = np.random.default_rng(1)
+    L = (rng.standard_normal((64, 16)) * 3).astype(np.float32)
+    for k in (1, 2, 4, 8, 16):
+        idx, w = O.route_topk(L, k)
+        assert np.allclose(w.sum(1), 1.0, atol=1e-14, rtol=0)
+        assert np.all(np.diff(w, axis=1) <= 0)              # descending logits -> descending weights
+        for t in range(0, 64, 7):
+            for a in range(k):
+                for b in range(k):
+                    r = math.exp(float(L[t, idx[t, a]]) - float(L[t, idx[t, b]]))
+                    assert w[t, a] / w[t, b] == pytest.approx(r, rel=1e-12)
+
+
+def test_gate_k2_closed_form():
+    rng = np.random.default_rng(2)
+    L = (rng.standard_normal((100, 8)) * 2).astype(np.float32)
+    idx, w = O.route_topk(L, 2)
+    for t in range(100):
+        d = float(L[t, idx[t, 0]]) - float(L[t, idx[t, 1]])
+        assert w[t, 0] == pytest.approx(1.0 / (1.0 + math.exp(-d)), rel=1e-14)   # sigma(L0 - L1)
+
+
+def test_gate_without_renormalisation_is_full_softmax():
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((50, 12)).astype(np.float32)
+    idx, w = O.route_topk(L, 3, renormalize=False)
+    full = scipy.special.softmax(L.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(full, idx.astype(np.int64), 1), rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# permutation / tile list
+# ---------------------------------------------------------------------------
+
+def test_permute_hand_example():
+    # T=5, k=2, experts 1..2 local (expert_begin=1, E_loc=2), tile_m=2, ranks [1,0,1,0,0].
+    # Local pairs sorted by (local expert, rank, token):
+    #   expert 1 (le0): (t1,j1,r0) (t3,j0,r0) (t0,j0,r1)  -> rows 0,1,2 ; row 3 pad
+    #   expert 2 (le1): (t1,j0,r0) (t3,j1,r0) (t2,j1,r1)  -> rows 4,5,6 ; row 7 pad
+    # Tiles (le, m): (0,0) last row 1 rank 0; (0,1) last real row 2 rank 1;
+    #                (1,0) last row 5 rank 0; (1,1) last real row 6 rank 1.
+    idx = np.array([[1, 3], [2, 1], [0, 2], [1, 2], [3, 0]])
+    ranks = np.array([1, 0, 1, 0, 0])
+    p = O.permute(idx, ranks, expert_begin=1, E_loc=2, tile_m=2)
+    assert list(p["counts"]) == [3, 3]
+    assert list(p["offsets"]) == [0, 4, 8]
+    assert list(p["row_src"]) == [3, 6, 0, -1, 2, 7, 5, -1]
+    assert list(p["row_rank"]) == [0, 0, 1, -1, 0, 0, 1, -1]
+    assert p["inv_perm"].tolist() == [[2, -1], [4, 0], [-1, 6], [1, 5], [-1, -1]]
+    assert p["tiles"] == [(0, 0), (1, 4), (0, 2), (1, 6)]
+    assert p["tile_prio"] == [0, 0, 1, 1]
+
+
+@pytest.mark.parametrize("T,k,E,e0,El,R,tm", [(300, 2, 8, 0, 8, 1, 16), (257, 6, 64, 0, 64, 1, 32),
+                                              (500, 8, 64, 8, 8, 8, 64), (33, 8, 256, 0, 256, 1, 16),
+                                              (128, 4, 8, 2, 3, 4, 8)])
+def test_permute_invariants(T, k, E, e0, El, R, tm):
+    rng = np.random.default_rng(T)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    idx, _ = O.route_topk(L, k)
+    ranks = rng.integers(0, R, size=T) if R > 1 else None
+    p = O.permute(idx, ranks, e0, El, tm)
+    rk = np.zeros(T, np.int64) if ranks is None else ranks
+    local = [(t, j) for t in range(T) for j in range(k) if e0 <= idx[t, j] < e0 + El]
+    # counts == bincount of local experts
+    assert np.array_equal(p["counts"], np.bincount(idx.ravel()[(idx.ravel() >= e0) & (idx.ravel() < e0 + El)] - e0,
+                                                   minlength=El))
+    # offsets are tile multiples and just big enough
+    off = p["offsets"]
+    assert off[0] == 0 and np.all(off % tm == 0)
+    assert np.array_equal(np.diff(off), -(-p["counts"] // tm) * tm)
+    # bijection local pairs <-> real rows, inverse consistent
+    real = np.nonzero(p["row_src"] >= 0)[0]
+    assert len(real) == len(local)
+    assert sorted(int(s) for s in p["row_src"][real]) == sorted(t * k + j for t, j in local)
+    for t, j in local:
+        assert p["row_src"][p["inv_perm"][t, j]] == t * k + j
+    for t in range(T):
+        for j in range(k):
+            if not e0 <= idx[t, j] < e0 + El:
+                assert p["inv_perm"][t, j] == -1
+    # same order as numpy lexsort on (expert, rank, token)
+    le = np.array([idx[t, j] - e0 for t, j in local])
+    tt = np.array([t for t, _ in local])
+    order = np.lexsort((tt, rk[tt], le))
+    expect = np.concatenate([np.arange(off[e], off[e] + p["counts"][e]) for e in range(El)]).astype(np.int64)
+    got = np.array([p["inv_perm"][local[i]] for i in order])
+    assert np.array_equal(got, expect)
+    # tiles cover each expert's real rows exactly once; priority = max rank in tile; order sorted
+    seen = []
+    for (e, b), pr in zip(p["tiles"], p["tile_prio"]):
+        rows = [r for r in range(b, b + tm) if p["row_src"][r] >= 0]
+        assert rows and all(off[e] <= r < off[e + 1] for r in rows)
+        assert pr == max(rk[p["row_src"][r] // k] for r in rows)
+        seen += rows
+    assert sorted(seen) == sorted(real.tolist())
+    keys = [(pr, e, b) for (e, b), pr in zip(p["tiles"], p["tile_prio"])]
+    assert keys == sorted(keys)
+
+
+def test_permute_exact_tile_multiple_has_no_padding():
+    # 32 tokens, top-1 over 2 experts, 16 tokens each: counts are exact tile multiples.
+    L = np.zeros((32, 2), np.float32)
+    L[:16, 0] = 1.0
+    L[16:, 1] = 1.0
+    idx, _ = O.route_topk(L, 1)
+    p = O.permute(idx, None, 0, 2, 16)
+    assert list(p["offsets"]) == [0, 16, 32]
+    assert list(p["row_src"]) == list(range(32))
+    assert p["tiles"] == [(0, 0), (1, 16)]
+
+
+def test_permute_no_ranks_is_expert_major():
+    rng = np.random.default_rng(9)
+    idx, _ = O.route_topk(rng.standard_normal((100, 8)).astype(np.float32), 2)
+    p = O.permute(idx, None, 0, 8, 16)
+    begins = [b for _, b in p["tiles"]]
+    assert begins == sorted(begins)                       # one rank: tiles in row order
+    assert set(p["tile_prio"]) == {0}
+
+
+# ---------------------------------------------------------------------------
+# expert FFN, combine and the whole layer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_single_expert_top1_is_dense_ffn(act):
+    rng = np.random.default_rng(4)
+    T, H, F = 12, 24, 40
+    X = rng.standard_normal((T, H))
+    ws = rand_weights(rng, 1, H, F, act)
+    L = rng.standard_normal((T, 1)).astype(np.float32)
+    out = O.moe_layer(X, L, 1, ws, act)
+    assert np.allclose(out, torch_ffn(X, ws[0], act), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("act,renorm", [("gelu", True), ("swiglu", True), ("swiglu", False)])
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 2), (3, 3), (4, 4)])
+def test_layer_matches_dense_mixture(act, renorm, E, k):
+    rng = np.random.default_rng(10 * E + k)
+    T, H, F = 8, 16, 32
+    X = rng.standard_normal((T, H))
+    L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # ties included
+    ws = rand_weights(rng, E, H, F, act)
+    out = O.moe_layer(X, L, k, ws, act, renormalize=renorm)
+    assert np.allclose(out, dense_mixture(X, L, k, ws, act, renormalize=renorm), rtol=1e-11, atol=1e-12)
+
+
+def test_top1_output_is_selected_expert():
+    rng = np.random.default_rng(5)
+    T, H, F, E = 10, 16, 24, 5
+    X = rng.standard_normal((T, H))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ws = rand_weights(rng, E, H, F, "swiglu")
+    out = O.moe_layer(X, L, 1, ws, "swiglu")
+    for t in range(T):
+        e = int(np.argmax(L[t]))
+        assert np.allclose(out[t], torch_ffn(X[t:t + 1], ws[e], "swiglu")[0], rtol=1e-12, atol=1e-12)
+
+
+def test_token_order_invariance():
+    rng = np.random.default_rng(6)
+    T, H, F, E, k = 16, 8, 16, 6, 2
+    X = rng.standard_normal((T, H))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ws = rand_weights(rng, E, H, F, "swiglu")
+    perm = rng.permutation(T)
+    a = O.moe_layer(X, L, k, ws, "swiglu")
+    b = O.moe_layer(X[perm], L[perm], k, ws, "swiglu")
+    assert np.allclose(a[perm], b, rtol=1e-13, atol=1e-14)
+
+
+def test_rank_partition_invariance():
+    # Expert parallelism (section 2.1): the shares of disjoint local expert ranges sum to the full layer.
+    rng = np.random.default_rng(7)
+    T, H, F, E, k = 20, 8, 12, 8, 3
+    X = rng.standard_normal((T, H))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ws = rand_weights(rng, E, H, F, "swiglu")
+    full = O.moe_layer(X, L, k, ws, "swiglu")
+    parts = sum(O.moe_layer(X, L, k, ws[e0:e0 + 2], "swiglu", expert_begin=e0, E_loc=2)
+                for e0 in range(0, E, 2))
+    assert np.allclose(parts, full, rtol=1e-12, atol=1e-13)
+
+
+def test_combine_and_permute_reassemble_the_layer():
+    # route -> permute -> per-row FFN -> combine equals the per-token loop.
+    rng = np.random.default_rng(8)
+    T, H, F, E, k, tm = 30, 8, 12, 6, 2, 4
+    X = rng.standard_normal((T, H))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ranks = rng.integers(0, 3, size=T)
+    ws = rand_weights(rng, E, H, F, "gelu")
+    idx, w = O.route_topk(L, k)
+    p = O.permute(idx, ranks, 1, 4, tm)
+    xp = O.gather_rows(X, p["row_src"], k)
+    y = np.zeros_like(xp)
+    for e in range(4):
+        for r in range(p["offsets"][e], p["offsets"][e] + p["counts"][e]):
+            y[r] = O.expert_ffn(xp[r], *ws[1 + e], "gelu")
+    out = O.combine(y, p["inv_perm"], w)
+    ref = O.moe_layer(X, L, k, ws[1:5], "gelu", expert_begin=1, E_loc=4)
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-14)
+    # tokens with no local slot give zero rows
+    none_local = [t for t in range(T) if not any(1 <= idx[t, j] < 5 for j in range(k))]
+    assert all(np.all(out[t] == 0) for t in none_local)
+
+
+def test_activation_closed_forms():
+    z = np.array([-30.0, -2.0, -0.5, 0.0, 0.5, 2.0, 30.0])
+    assert np.allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-15, atol=1e-300)
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    # GELU(x) = x * Phi(x): compare with the normal CDF from scipy
+    assert np.allclose(O.gelu(z), z * scipy.special.ndtr(z), rtol=1e-14, atol=1e-15)
