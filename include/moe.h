@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of libmoe.so: one GPU's share of a Mixture-of-Experts layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as "Comet: Fine-grained Computation-communication Overlapping for
+ * Mixture-of-Experts" (paperlayer.ai summary) states it in section 2.1 (MoE
+ * Structure), routes every token to its top-k experts, runs each selected
+ * expert's feed-forward network on it, and gathers and reduces the expert
+ * outputs over the k choices.  The four calls below are the steps of that
+ * path, in order:
+ *
+ *   moe_route_topk   top-k routing and gate weights
+ *   moe_permute      reorganisation into expert-contiguous, tile-aligned rows
+ *   moe_grouped_ffn  layer0 grouped GEMM + activation, layer1 grouped GEMM
+ *   moe_combine      top-k weighted reduce back to token order
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise, and
+ *     must be 16-byte aligned.  The caller owns all memory: the library never
+ *     allocates, frees or synchronises.  Work is enqueued on `stream` (a
+ *     hipStream_t passed as void*; NULL = the default stream) and the call
+ *     returns without waiting.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns its code and enqueues nothing.  Device-side faults
+ *     surface at the caller's next synchronisation.  T == 0 returns MOE_OK and
+ *     launches nothing.  No C++ exception crosses this interface.
+ *   - Data-dependent sizes (rows per expert, number of tiles) stay on the
+ *     device; capacities are host formulas (moe_rows_capacity,
+ *     moe_tiles_capacity), so the four calls can be enqueued back to back
+ *     without any device-to-host copy.
+ *   - bf16 arguments are passed as void* and hold IEEE bfloat16 values.
+ *   - Calls are stateless and re-entrant; concurrent calls on different
+ *     streams must not share output or workspace buffers.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, misalignment, negative or inconsistent size */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement (e.g. H % 64) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_permute_workspace_bytes() */
+  MOE_ERR_LAUNCH = 4       /* the HIP runtime reported an error when launching */
+} moe_status;
+
+typedef enum {
+  MOE_ACT_GELU = 0,  /* a = gelu(x.W1), exact erf form; y = a.W2 */
+  MOE_ACT_SWIGLU = 1 /* a = silu(x.Wg) * (x.Wu), silu(z) = z/(1+e^-z); y = a.Wd */
+} moe_act;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(int status);
+
+/* Library ABI version (incremented on any signature change). */
+int32_t moe_abi_version(void);
+
+/* R_cap: rows of the reorganised buffers (x_perm, act_buf, y_perm) for T
+ * tokens, top-k, E_loc local experts and row tile tile_m:
+ *   T * min(k, E_loc) + E_loc * (tile_m - 1).
+ * Returns -1 on invalid arguments. */
+int64_t moe_rows_capacity(int64_t T, int32_t k, int32_t E_loc, int32_t tile_m);
+
+/* Capacity of the tile list: floor(T * min(k, E_loc) / tile_m) + E_loc
+ * (each tile is two int32).  Returns -1 on invalid arguments. */
+int64_t moe_tiles_capacity(int64_t T, int32_t k, int32_t E_loc, int32_t tile_m);
+
+/* Bytes of device workspace moe_permute needs.  Returns 0 on invalid arguments. */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E_loc, int32_t num_ranks);
+
+/*
+ * moe_route_topk -- top-k routing (section 2.1: each token activates only the
+ * experts its router selects; the gate weights weight the top-k reduce).
+ *
+ *   logits      [T, E] fp32, row-major; finite values (precondition).
+ *   topk_idx    [T, k] int32 out: expert ids of token t in descending logit
+ *               order; equal logits are taken lower id first.
+ *   topk_w      [T, k] fp32 out: renormalize != 0 -> softmax over the k
+ *               selected logits (each row sums to 1); renormalize == 0 ->
+ *               full softmax over all E evaluated at the selected experts.
+ * Requires 1 <= k <= E, E <= 1024, k <= 32.
+ */
+moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                          int32_t renormalize, int32_t* topk_idx, float* topk_w,
+                          void* stream);
+
+/*
+ * moe_permute -- token reorganisation into expert-contiguous, tile-aligned
+ * sub-tensors (section 3.1.2: sub-tensors are regrouped into GEMM tiles;
+ * layer0 sorts tokens by source rank and prioritises tiles with local
+ * tokens; section 2.2.1: reorganisation exposes only the data a tile needs).
+ *
+ * The (token t, slot j) pairs whose expert e = topk_idx[t, j] lies in the
+ * local range [expert_begin, expert_begin + E_loc) are sorted by
+ * (e - expert_begin, src_rank[t], t); each local expert's rows are padded up
+ * to a multiple of tile_m.  Outputs:
+ *   x_perm          [R_cap, H] bf16: row p = x[row_src[p] / k]; padding rows
+ *                   are left untouched (their content is unspecified).
+ *   expert_counts   [E_loc] int32: real rows per local expert.
+ *   expert_offsets  [E_loc + 1] int32: padded first row of each expert.
+ *   row_src         [R_cap] int32: t * k + j of a real row, -1 otherwise.
+ *   inv_perm        [T, k] int32: row of pair (t, j), -1 if not local.
+ *   tiles           [tiles_cap, 2] int32: (local expert, first row) of every
+ *                   row tile, ordered by (priority, expert, tile index) where
+ *                   a tile's priority is the largest source rank among its rows.
+ *   num_tiles       [1] int32: number of valid entries in tiles.
+ * Inputs: x [T, H] bf16; topk_idx [T, k] int32 (from moe_route_topk, or any
+ * ids in [0, E) with no repeat within a row); src_rank [T] int32 with values
+ * in [0, num_ranks), or NULL = every token is local (rank 0).
+ * ws / ws_bytes: device scratch of at least moe_permute_workspace_bytes().
+ * Requires H % 8 == 0, tile_m in {16, 32, 64, 128, 256},
+ * E_loc * num_ranks <= 4096, num_ranks <= 64, k <= 32.
+ */
+moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* src_rank,
+                       int64_t T, int32_t H, int32_t k, int32_t E, int32_t expert_begin,
+                       int32_t E_loc, int32_t num_ranks, int32_t tile_m,
+                       void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* row_src, int32_t* inv_perm, int32_t* tiles,
+                       int32_t* num_tiles, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- the experts' feed-forward networks as two grouped GEMMs
+ * over all local experts (section 3.1.2: one GroupGEMM covers the experts of
+ * this rank; section 3.1.1: layer0 is decomposed along M (token rows),
+ * layer1 along N (output columns), because the top-k reduce couples rows
+ * across experts; tile-level-signalling follow-up, abstract: one persistent
+ * kernel covers all local experts).
+ *
+ *   layer0:  act_buf[p, :] = act( x_perm[p, :] . W0[e] (, x_perm[p, :] . W0u[e]) )
+ *   layer1:  y_perm[p, :]  = act_buf[p, :] . W1[e]
+ * for every real row p of every local expert e.  Weights are stored
+ * output-major (each stored matrix is the transpose of the mathematical one,
+ * so the reduction dimension is contiguous):
+ *   w0      [E_loc, F, H] bf16: W_gate^T (SwiGLU) or W1^T (GELU)
+ *   w0_up   [E_loc, F, H] bf16: W_up^T (SwiGLU); must be NULL for GELU
+ *   w1      [E_loc, H, F] bf16: W_down^T (SwiGLU) or W2^T (GELU)
+ *   act_buf [R_cap, F] bf16 out: the activation, rounded to nearest even.
+ *   y_perm  [R_cap, H] fp32 out.
+ * Only real rows are written; padding rows of act_buf and y_perm are left
+ * untouched.  x_perm, expert_counts, expert_offsets, tiles and num_tiles are
+ * moe_permute's outputs for the same tile_m; R_cap and tiles_cap are the
+ * capacities they were allocated with.  Accumulation is fp32.
+ * Requires H % 128 == 0, F % 128 == 0, tile_m in {16, 32, 64, 128, 256}.
+ */
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
+                           const int32_t* expert_offsets, const int32_t* tiles,
+                           const int32_t* num_tiles, const void* w0, const void* w0_up,
+                           const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act,
+                           int32_t tile_m, int64_t R_cap, int64_t tiles_cap,
+                           void* act_buf, float* y_perm, void* stream);
+
+/*
+ * moe_combine -- gather and top-k reduce (section 2.1: expert outputs are
+ * gathered back to their tokens and reduced over the top-k choices).
+ *
+ *   out[t, :] = sum over j = 0..k-1 with inv_perm[t, j] >= 0 of
+ *               topk_w[t, j] * y_perm[inv_perm[t, j], :]
+ * summed in slot order in fp32; a token with no local slot gets a zero row.
+ *   y_perm  [R_cap, H] fp32;  inv_perm [T, k] int32 (values < R_cap or -1);
+ *   topk_w  [T, k] fp32;      out [T, H] fp32 out.
+ * Requires H % 4 == 0.
+ */
+moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       int64_t T, int32_t k, int32_t H, int64_t R_cap, float* out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

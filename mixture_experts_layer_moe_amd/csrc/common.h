@@ -1,0 +1,58 @@
+// Shared device helpers and internal launcher declarations for libmoe.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int intx4;
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------------------
+// Internal launchers (implemented in the .hip files; called by moe_api.hip
+// after argument validation).  All return hipGetLastError() after launching.
+// ---------------------------------------------------------------------------
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+                             int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+struct PermuteArgs {
+  const uint16_t* x;
+  const int32_t* topk_idx;
+  const int32_t* src_rank;  // may be null
+  int64_t T;
+  int H, k, E, expert_begin, E_loc, num_ranks, tile_m;
+  int64_t R_cap, tiles_cap;
+  uint16_t* x_perm;
+  int32_t *counts, *offsets, *row_src, *inv_perm, *tiles, *num_tiles;
+  void* ws;
+};
+size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct FfnArgs {
+  const uint16_t* x_perm;
+  const int32_t *counts, *offsets, *tiles, *num_tiles;
+  const uint16_t *w0, *w0_up, *w1;
+  int E_loc, H, F, act, tile_m;
+  int64_t R_cap, tiles_cap;
+  uint16_t* act_buf;
+  float* y_perm;
+};
+hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                          int64_t T, int k, int H, int64_t R_cap, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,318 @@
+// Token reorganisation into expert-contiguous, tile-aligned sub-tensors.
+//
+// "Comet: Fine-grained Computation-communication Overlapping for
+// Mixture-of-Experts", section 3.1.2: the decomposed shared tensor is
+// regrouped into GEMM-tile-aligned sub-tensors; layer0 sorts tokens by source
+// rank and prioritises tiles holding local tokens.  Section 2.2.1: data
+// reorganisation exposes only the data each tile needs.
+//
+// The (token, slot) pairs of local experts are stably counting-sorted on the
+// bucket key b = local_expert * num_ranks + src_rank, visiting pairs in token
+// order, which yields the order (expert, rank, token).  Three launches, no
+// atomics deciding any order (the result is bit-identical run to run):
+//   A  hist:    one wavefront per 64-token chunk c; for every bucket b a
+//               ballot gives each pair its rank inside (b, c) and the count
+//               hist[b][c].
+//   B  scan:    one block: exclusive scan of hist in (b, c) order, per-expert
+//               counts, tile-padded offsets, the base row of every (b, c),
+//               padding markers in row_src, and the tile list ordered by
+//               (priority, expert, m-tile) with a stable partition on priority.
+//   D  scatter: one wavefront per token: row of each local pair =
+//               base[b][c] + rank, written to row_src / inv_perm, and the
+//               token's row copied once from HBM to each of its rows in
+//               16-byte chunks.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 64;          // tokens per chunk (one wavefront)
+constexpr int kScanThreads = 1024;  // block size of kernel B
+constexpr int kMaxExperts = 4096;   // E_loc * num_ranks <= 4096 (validated on the host)
+
+struct WsLayout {
+  int64_t nb, nc;
+  int32_t* hist;   // [nb * nc]
+  int32_t* lrank;  // [T * k]
+};
+
+__host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+__host__ __device__ inline WsLayout ws_layout(void* ws, int64_t T, int k, int E_loc, int num_ranks) {
+  WsLayout L;
+  L.nb = (int64_t)E_loc * num_ranks;
+  L.nc = (T + kChunk - 1) / kChunk;
+  char* p = static_cast<char*>(ws);
+  L.hist = reinterpret_cast<int32_t*>(p);
+  p += align_up(L.nb * L.nc * 4, 256);
+  L.lrank = reinterpret_cast<int32_t*>(p);
+  return L;
+}
+
+__device__ __forceinline__ int clamp_rank(const int32_t* src_rank, int64_t t, int R) {
+  if (src_rank == nullptr) return 0;
+  const int r = src_rank[t];
+  return r < 0 ? 0 : (r >= R ? R - 1 : r);
+}
+
+// ---------------------------------------------------------------------------
+// A: per-chunk bucket counts and in-chunk stable ranks
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                           const int32_t* __restrict__ src_rank,
+                                                           int64_t T, int k, int expert_begin,
+                                                           int E_loc, int R, int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ lrank, int64_t nb,
+                                                           int64_t nc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (c >= nc) return;
+  const int64_t t = c * kChunk + lane;
+  const bool valid = t < T;
+  const int r = valid ? clamp_rank(src_rank, t, R) : 0;
+
+  int bucket[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    bucket[j] = -1;
+    if (j < k && valid) {
+      const int le = topk_idx[t * k + j] - expert_begin;
+      if (le >= 0 && le < E_loc) bucket[j] = le * R + r;
+      else lrank[t * k + j] = -1;
+    }
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t b = 0; b < nb; ++b) {
+    int jj = -1;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < k && bucket[j] == (int)b) jj = j;
+    const uint64_t m = __ballot(jj >= 0);
+    if (jj >= 0) lrank[t * k + jj] = __popcll(m & lt);
+    if (lane == 0) hist[b * nc + c] = __popcll(m);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide scan helpers for kernel B (1024 threads = 16 wavefronts)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of one int per thread over the block; returns the prefix and
+// writes the block total to *total.  Contains __syncthreads().
+__device__ int block_excl_scan(int v, int* sh /*[16 + 1]*/, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < 16 ? sh[lane] : 0;
+    const int si = wave_incl_scan(s);
+    if (lane < 16) sh[lane] = si - s;
+    if (lane == 15) sh[16] = si;
+  }
+  __syncthreads();
+  const int res = sh[w] + inc - v;
+  *total = sh[16];
+  __syncthreads();
+  return res;
+}
+
+// ---------------------------------------------------------------------------
+// B: scan, offsets, padding markers, tile list
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
+    int32_t* __restrict__ hist, int64_t nb, int64_t nc, int E_loc, int R, int tile_m, int64_t R_cap,
+    int64_t tiles_cap, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int sh[17];
+  __shared__ int s_us[kMaxExperts + 1];   // unpadded start of each expert
+  __shared__ int s_off[kMaxExperts + 1];  // padded start
+  __shared__ int s_tb[kMaxExperts + 1];   // first tile index of each expert
+  const int tid = threadIdx.x;
+  const int64_t N = nb * nc;
+
+  // 1. exclusive scan of hist in (bucket, chunk) order
+  const int64_t seg = (N + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = (int64_t)tid * seg, hi = lo + seg < N ? lo + seg : N;
+  int s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += hist[i];
+  int total;
+  int run = block_excl_scan(s, sh, &total);
+  for (int64_t i = lo; i < hi; ++i) {
+    const int h = hist[i];
+    hist[i] = run;
+    run += h;
+  }
+  __syncthreads();
+
+  // 2. per-expert unpadded starts, counts, padded offsets, tile starts
+  for (int le = tid; le <= E_loc; le += kScanThreads)
+    s_us[le] = le < E_loc ? hist[(int64_t)le * R * nc] : total;
+  __syncthreads();
+  {
+    // E_loc <= 4096 -> at most 4 experts per thread, contiguous.
+    const int per = (E_loc + kScanThreads - 1) / kScanThreads;
+    const int e_lo = tid * per, e_hi = e_lo + per < E_loc ? e_lo + per : E_loc;
+    int pad_sum = 0, tile_sum = 0;
+    for (int le = e_lo; le < e_hi; ++le) {
+      const int cnt = s_us[le + 1] - s_us[le];
+      const int mt = (cnt + tile_m - 1) / tile_m;
+      pad_sum += mt * tile_m;
+      tile_sum += mt;
+    }
+    int pad_total, tile_total;
+    int pad_run = block_excl_scan(pad_sum, sh, &pad_total);
+    int tile_run = block_excl_scan(tile_sum, sh, &tile_total);
+    for (int le = e_lo; le < e_hi; ++le) {
+      const int cnt = s_us[le + 1] - s_us[le];
+      const int mt = (cnt + tile_m - 1) / tile_m;
+      s_off[le] = pad_run;
+      s_tb[le] = tile_run;
+      counts[le] = cnt;
+      offsets[le] = pad_run;
+      pad_run += mt * tile_m;
+      tile_run += mt;
+    }
+    if (tid == 0) {
+      s_off[E_loc] = pad_total;
+      s_tb[E_loc] = tile_total;
+      offsets[E_loc] = pad_total;
+    }
+  }
+  __syncthreads();
+
+  // 3. base row of every (bucket, chunk): padded start + rank inside expert
+  for (int64_t i = tid; i < N; i += kScanThreads) {
+    const int le = (int)(i / nc / R);
+    hist[i] = s_off[le] + hist[i] - s_us[le];
+  }
+
+  // 4. padding rows and the unused tail carry -1 in row_src
+  for (int64_t i = tid; i < (int64_t)E_loc * tile_m; i += kScanThreads) {
+    const int le = (int)(i / tile_m), q = (int)(i % tile_m);
+    const int64_t row = (int64_t)s_off[le] + (s_us[le + 1] - s_us[le]) + q;
+    if (row < s_off[le + 1]) row_src[row] = -1;
+  }
+  for (int64_t row = (int64_t)s_off[E_loc] + tid; row < R_cap; row += kScanThreads) row_src[row] = -1;
+  __syncthreads();  // hist now holds base rows; step 5 reads them
+
+  // 5. tile list, stably partitioned on priority (= rank of the tile's last row)
+  const int nt = s_tb[E_loc] < tiles_cap ? s_tb[E_loc] : (int)tiles_cap;
+  if (tid == 0) *num_tiles = nt;
+  int placed = 0;
+  for (int p = 0; p < R; ++p) {
+    for (int base_i = 0; base_i < nt; base_i += kScanThreads) {
+      const int i = base_i + tid;
+      int le = 0, prio = -1, m = 0;
+      if (i < nt) {
+        int a = 0, b = E_loc;  // largest le with s_tb[le] <= i
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (s_tb[mid] <= i) a = mid; else b = mid;
+        }
+        le = a;
+        m = i - s_tb[le];
+        const int cnt = s_us[le + 1] - s_us[le];
+        const int last = ((m + 1) * tile_m < cnt ? (m + 1) * tile_m : cnt) - 1;
+        prio = 0;
+        for (int r = 1; r < R; ++r) {
+          const int cum = hist[((int64_t)le * R + r) * nc] - s_off[le];
+          if (cum <= last) prio = r;
+        }
+      }
+      const int flag = (prio == p) ? 1 : 0;
+      int cnt_p;
+      const int pos = block_excl_scan(flag, sh, &cnt_p);
+      if (flag) {
+        tiles[2 * (int64_t)(placed + pos)] = le;
+        tiles[2 * (int64_t)(placed + pos) + 1] = s_off[le] + m * tile_m;
+      }
+      placed += cnt_p;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D: index scatter + row copy, one wavefront per token
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const intx4* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ src_rank, int64_t T, int H, int k, int expert_begin, int E_loc, int R,
+    int64_t R_cap, const int32_t* __restrict__ base, const int32_t* __restrict__ lrank, int64_t nc,
+    intx4* __restrict__ x_perm, int32_t* __restrict__ row_src, int32_t* __restrict__ inv_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int p = -1;
+  if (lane < k) {
+    const int le = topk_idx[t * k + lane] - expert_begin;
+    if (le >= 0 && le < E_loc) {
+      const int r = clamp_rank(src_rank, t, R);
+      const int64_t b = (int64_t)le * R + r;
+      p = base[b * nc + t / kChunk] + lrank[t * k + lane];
+      if (p >= R_cap) p = -1;  // inconsistent input; never write out of bounds
+      if (p >= 0) row_src[p] = (int32_t)(t * k + lane);
+    }
+    inv_perm[t * k + lane] = p;
+  }
+  // Destination rows of this token's k slots (-1 = not local), wave-uniform.
+  int dst[32];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    dst[j] = j < k ? __shfl(p, j) : -1;
+    any |= dst[j] >= 0;
+  }
+  if (!any) return;
+  const int nch = H / 8;  // 16-byte chunks per row
+  const intx4* src = x + t * nch;
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < nch; c0 += kWave * U) {
+    intx4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u * kWave < nch) v[u] = src[c0 + u * kWave];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (dst[j] < 0) continue;
+      intx4* out = x_perm + (int64_t)dst[j] * nch;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * kWave < nch) out[c0 + u * kWave] = v[u];
+    }
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks) {
+  const int64_t nb = (int64_t)E_loc * num_ranks, nc = (T + kChunk - 1) / kChunk;
+  return (size_t)(align_up(nb * nc * 4, 256) + align_up(T * k * 4, 256));
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  WsLayout L = ws_layout(a.ws, a.T, a.k, a.E_loc, a.num_ranks);
+  const int wpb = 4;  // wavefronts per block
+  hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)((L.nc + wpb - 1) / wpb)), dim3(wpb * kWave), 0, s,
+                     a.topk_idx, a.src_rank, a.T, a.k, a.expert_begin, a.E_loc, a.num_ranks, L.hist,
+                     L.lrank, L.nb, L.nc);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, L.hist, L.nb, L.nc, a.E_loc,
+                     a.num_ranks, a.tile_m, a.R_cap, a.tiles_cap, a.counts, a.offsets, a.row_src, a.tiles,
+                     a.num_tiles);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((a.T + wpb - 1) / wpb)), dim3(wpb * kWave), 0, s,
+                     reinterpret_cast<const intx4*>(a.x), a.topk_idx, a.src_rank, a.T, a.H, a.k,
+                     a.expert_begin, a.E_loc, a.num_ranks, a.R_cap, L.hist, L.lrank, L.nc,
+                     reinterpret_cast<intx4*>(a.x_perm), a.row_src, a.inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+// Top-k routing with renormalised gate weights.
+//
+// "Comet: Fine-grained Computation-communication Overlapping for
+// Mixture-of-Experts", section 2.1 (MoE Structure): each token activates only
+// the experts its router selects, and the gate weights weight the top-k
+// reduce.  Gate = softmax over the k selected logits (full softmax
+// renormalised over the top-k).
+//
+// One wavefront per token.  Lane l holds logits e = l, l+64, ... (E <= 1024,
+// so at most 16 per lane).  k rounds of a wave-wide arg-max on the key
+// (value desc, id asc) select the experts in slot order; the comparisons are
+// exact, so the ids are bit-identical to any correct sort with that key.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxPerLane = 16;  // E <= 1024
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t T, int E, int k, int renormalize,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+  const float* row = logits + t * (int64_t)E;
+
+  float v[kMaxPerLane];
+  const int per_lane = (E + kWave - 1) / kWave;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    v[i] = (i < per_lane && e < E) ? row[e] : -__builtin_inff();
+  }
+  uint32_t taken = 0;  // bit i set: v[i] already selected (or absent)
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i)
+    if (!(i < per_lane && lane + i * kWave < E)) taken |= 1u << i;
+
+  float top = 0.f, sel_v = 0.f;
+  int sel_i = 0;
+  float zsum = 0.f;
+  // Slot results are kept by lane j (j < k <= 32).
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      if (!(taken & (1u << i)) && better(v[i], lane + i * kWave, bv, bi)) {
+        bv = v[i];
+        bi = lane + i * kWave;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    // bv, bi are now wave-uniform: the j-th expert of this token.
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (j == 0) top = bv;
+    const float z = expf(bv - top);
+    zsum += z;
+    if (lane == j) {
+      sel_v = bv;
+      sel_i = bi;
+    }
+  }
+  float denom = zsum;
+  if (!renormalize) {
+    // Full softmax denominator over all E logits.
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + i * kWave;
+      if (i < per_lane && e < E) s += expf(v[i] - top);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    denom = s;
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = sel_i;
+    topk_w[t * k + lane] = expf(sel_v - top) / denom;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int renormalize,
+                             int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  constexpr int kTokensPerBlock = 4;
+  const int64_t blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)blocks), dim3(kTokensPerBlock * kWave), 0, s,
+                     logits, T, E, k, renormalize, topk_idx, topk_w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,209 @@
+"""ctypes binding of libmoe.so.
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device memory and the stream; nothing here computes.  If
+the library is missing, loading raises -- there is no fallback.
+
+The functions carry the C names (see include/moe.h for the operations,
+layouts and error codes).  Output tensors may be passed in (to reuse
+buffers, e.g. under graph capture) or are allocated on the input's device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_ACT_GELU = 0
+MOE_ACT_SWIGLU = 1
+ACTS = {"gelu": MOE_ACT_GELU, "swiglu": MOE_ACT_SWIGLU}
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_abi_version": (_i32, []),
+    "moe_rows_capacity": (_i64, [_i64, _i32, _i32, _i32]),
+    "moe_tiles_capacity": (_i64, [_i64, _i32, _i32, _i32]),
+    "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_permute": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_grouped_ffn": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                       _i64, _i64, _p, _p, _p]),
+    "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i64, _p, _p]),
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {lib().moe_status_str(status).decode()} ({status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built by mixture_experts_layer_moe_amd.build); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m mixture_experts_layer_moe_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def _need(t: torch.Tensor, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rows_capacity(T: int, k: int, E_loc: int, tile_m: int) -> int:
+    return int(lib().moe_rows_capacity(T, k, E_loc, tile_m))
+
+
+def tiles_capacity(T: int, k: int, E_loc: int, tile_m: int) -> int:
+    return int(lib().moe_tiles_capacity(T, k, E_loc, tile_m))
+
+
+def permute_workspace_bytes(T: int, k: int, E_loc: int, num_ranks: int) -> int:
+    return int(lib().moe_permute_workspace_bytes(T, k, E_loc, num_ranks))
+
+
+# ---------------------------------------------------------------------------
+# the four calls
+# ---------------------------------------------------------------------------
+
+def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True,
+                   topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                   stream=None):
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)),
+                                                  _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+    return topk_idx, topk_w
+
+
+@dataclass
+class Permuted:
+    """Outputs of moe_permute (all device tensors; counts stay on the device)."""
+    x_perm: torch.Tensor          # [R_cap, H] bf16
+    expert_counts: torch.Tensor   # [E_loc] int32
+    expert_offsets: torch.Tensor  # [E_loc + 1] int32
+    row_src: torch.Tensor         # [R_cap] int32
+    inv_perm: torch.Tensor        # [T, k] int32
+    tiles: torch.Tensor           # [tiles_cap, 2] int32
+    num_tiles: torch.Tensor       # [1] int32
+    tile_m: int
+    R_cap: int
+    tiles_cap: int
+
+
+def alloc_permuted(T: int, H: int, k: int, E_loc: int, tile_m: int, device) -> Permuted:
+    R_cap = rows_capacity(T, k, E_loc, tile_m)
+    tcap = tiles_capacity(T, k, E_loc, tile_m)
+    i32 = dict(dtype=torch.int32, device=device)
+    return Permuted(
+        x_perm=torch.empty((R_cap, H), dtype=torch.bfloat16, device=device),
+        expert_counts=torch.empty(E_loc, **i32), expert_offsets=torch.empty(E_loc + 1, **i32),
+        row_src=torch.empty(R_cap, **i32), inv_perm=torch.empty((T, k), **i32),
+        tiles=torch.empty((tcap, 2), **i32), num_tiles=torch.empty(1, **i32),
+        tile_m=tile_m, R_cap=R_cap, tiles_cap=tcap)
+
+
+def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, src_rank: Optional[torch.Tensor], E: int,
+                expert_begin: int, E_loc: int, num_ranks: int, tile_m: int,
+                out: Optional[Permuted] = None, ws: Optional[torch.Tensor] = None,
+                stream=None) -> Permuted:
+    _need(x, torch.bfloat16, "x")
+    _need(topk_idx, torch.int32, "topk_idx")
+    if src_rank is not None:
+        _need(src_rank, torch.int32, "src_rank")
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    if out is None:
+        out = alloc_permuted(T, H, k, E_loc, tile_m, x.device)
+    nbytes = permute_workspace_bytes(T, k, E_loc, num_ranks)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check("moe_permute", lib().moe_permute(
+        _ptr(x), _ptr(topk_idx), _ptr(src_rank), T, H, k, E, expert_begin, E_loc, num_ranks, tile_m,
+        _ptr(out.x_perm), _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.row_src),
+        _ptr(out.inv_perm), _ptr(out.tiles), _ptr(out.num_tiles), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_grouped_ffn(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor], w1: torch.Tensor,
+                    act: str, act_buf: Optional[torch.Tensor] = None,
+                    y_perm: Optional[torch.Tensor] = None, stream=None):
+    _need(w0, torch.bfloat16, "w0")
+    _need(w1, torch.bfloat16, "w1")
+    if w0_up is not None:
+        _need(w0_up, torch.bfloat16, "w0_up")
+    E_loc, F, H = w0.shape
+    dev = w0.device
+    if act_buf is None:
+        act_buf = torch.empty((p.R_cap, F), dtype=torch.bfloat16, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty((p.R_cap, H), dtype=torch.float32, device=dev)
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(
+        _ptr(p.x_perm), _ptr(p.expert_counts), _ptr(p.expert_offsets), _ptr(p.tiles), _ptr(p.num_tiles),
+        _ptr(w0), _ptr(w0_up), _ptr(w1), E_loc, H, F, ACTS[act], p.tile_m, p.R_cap, p.tiles_cap,
+        _ptr(act_buf), _ptr(y_perm), _stream(stream)))
+    return act_buf, y_perm
+
+
+def moe_combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, topk_w: torch.Tensor,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _need(y_perm, torch.float32, "y_perm")
+    _need(inv_perm, torch.int32, "inv_perm")
+    _need(topk_w, torch.float32, "topk_w")
+    T, k = inv_perm.shape
+    R_cap, H = y_perm.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=y_perm.device)
+    _check("moe_combine", lib().moe_combine(_ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), T, k, H, R_cap,
+                                            _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,63 @@
+"""One GPU's share of an MoE layer: the four library calls on preallocated buffers.
+
+Marshalling only: buffers are allocated once with torch, and `run()` enqueues
+moe_route_topk -> moe_permute -> moe_grouped_ffn -> moe_combine on one stream
+with no host synchronisation in between (every data-dependent size stays on
+the device), so the whole layer can also be captured in a HIP graph.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import ffi
+from .workloads import MoEConfig
+
+
+class MoELayer:
+    def __init__(self, cfg: MoEConfig, x: torch.Tensor, logits: torch.Tensor,
+                 src_rank: Optional[torch.Tensor], w0: torch.Tensor, w0_up: Optional[torch.Tensor],
+                 w1: torch.Tensor, tile_m: Optional[int] = None, renormalize: bool = True):
+        self.cfg = cfg
+        self.tile_m = tile_m or cfg.tile_m
+        self.renormalize = renormalize
+        self.x, self.logits, self.src_rank = x, logits, src_rank
+        self.w0, self.w0_up, self.w1 = w0, w0_up, w1
+        dev = x.device
+        T, H, k, El = cfg.T, cfg.H, cfg.k, cfg.n_local
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.perm = ffi.alloc_permuted(T, H, k, El, self.tile_m, dev)
+        nbytes = ffi.permute_workspace_bytes(T, k, El, cfg.num_ranks)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.act_buf = torch.empty((self.perm.R_cap, cfg.F), dtype=torch.bfloat16, device=dev)
+        self.y_perm = torch.empty((self.perm.R_cap, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    @classmethod
+    def from_inputs(cls, cfg: MoEConfig, inputs: dict, **kw) -> "MoELayer":
+        return cls(cfg, inputs["x"], inputs["logits"], inputs["src_rank"], inputs["w0"],
+                   inputs["w0_up"], inputs["w1"], **kw)
+
+    def route(self, stream=None):
+        ffi.moe_route_topk(self.logits, self.cfg.k, self.renormalize, self.topk_idx, self.topk_w, stream)
+
+    def permute(self, stream=None):
+        c = self.cfg
+        ffi.moe_permute(self.x, self.topk_idx, self.src_rank, c.E, c.expert_begin, c.n_local,
+                        c.num_ranks, self.tile_m, out=self.perm, ws=self.ws, stream=stream)
+
+    def ffn(self, stream=None):
+        ffi.moe_grouped_ffn(self.perm, self.w0, self.w0_up, self.w1, self.cfg.act,
+                            self.act_buf, self.y_perm, stream)
+
+    def combine(self, stream=None):
+        ffi.moe_combine(self.y_perm, self.perm.inv_perm, self.topk_w, self.out, stream)
+
+    def run(self, stream=None) -> torch.Tensor:
+        self.route(stream)
+        self.permute(stream)
+        self.ffn(stream)
+        self.combine(stream)
+        return self.out

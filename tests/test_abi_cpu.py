@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: symbols, capacity formulas, host-side validation codes.
+
+No call here reaches a kernel launch: each one returns from host validation
+(or is a pure host helper), so this runs on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_moe_amd import ffi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ffi.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert {"moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libmoe.so does not export {n}"
+        assert n in ffi._SIGNATURES, f"binding has no signature for {n}"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
+                       (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_LAUNCH"), (99, b"MOE_ERR_UNKNOWN")]:
+        assert L.moe_status_str(code) == name
+
+
+@pytest.mark.parametrize("T,k,El,tm", [(4096, 2, 8, 256), (16384, 8, 8, 256), (64, 8, 256, 16),
+                                       (1, 1, 1, 16), (0, 2, 8, 64), (100, 4, 2, 32)])
+def test_capacities(T, k, El, tm):
+    assert ffi.rows_capacity(T, k, El, tm) == T * min(k, El) + El * (tm - 1)
+    assert ffi.tiles_capacity(T, k, El, tm) == T * min(k, El) // tm + El
+    assert ffi.permute_workspace_bytes(T, k, El, 8) >= 4 * (T * k)
+
+
+def test_capacity_bounds_hold_for_worst_case_routing():
+    # Sum over experts of ceil(c_e / tm) * tm <= R_cap and of ceil(c_e / tm) <= tiles_cap
+    # for every split of R <= T*min(k,E_loc) rows over E_loc experts (checked on extreme splits).
+    import itertools
+    T, k, El, tm = 100, 3, 4, 16
+    R_max = T * min(k, El)
+    for split in [(T, T, T, 0), (T, T, 99, 1), (17, 17, 17, T), (1, 1, 1, T), (97, 97, 97, 9), (0, 0, 0, 0)]:
+        assert sum(split) <= R_max and max(split) <= T
+        rows = sum(-(-c // tm) * tm for c in split)
+        tiles = sum(-(-c // tm) for c in split)
+        assert rows <= ffi.rows_capacity(T, k, El, tm)
+        assert tiles <= ffi.tiles_capacity(T, k, El, tm)
+    assert ffi.rows_capacity(-1, 2, 8, 16) == -1
+    assert ffi.tiles_capacity(10, 0, 8, 16) == -1
+
+
+NULL = None
+FAKE = ctypes.c_void_p(16 * 1024)   # aligned, never dereferenced: validation fails first
+
+
+def test_route_validation(L):
+    assert L.moe_route_topk(FAKE, 10, 8, 0, 1, FAKE, FAKE, NULL) == INVALID        # k < 1
+    assert L.moe_route_topk(FAKE, 10, 8, 9, 1, FAKE, FAKE, NULL) == INVALID        # k > E
+    assert L.moe_route_topk(FAKE, -1, 8, 2, 1, FAKE, FAKE, NULL) == INVALID        # T < 0
+    assert L.moe_route_topk(FAKE, 10, 2048, 2, 1, FAKE, FAKE, NULL) == UNSUPPORTED  # E > 1024
+    assert L.moe_route_topk(FAKE, 10, 64, 33, 1, FAKE, FAKE, NULL) == UNSUPPORTED  # k > 32
+    assert L.moe_route_topk(NULL, 10, 8, 2, 1, FAKE, FAKE, NULL) == INVALID        # null
+    assert L.moe_route_topk(ctypes.c_void_p(16 * 1024 + 4), 10, 8, 2, 1, FAKE, FAKE, NULL) == INVALID  # misaligned
+    assert L.moe_route_topk(NULL, 0, 8, 2, 1, NULL, NULL, NULL) == OK              # T == 0: nothing to do
+
+
+def permute_call(L, **over):
+    a = dict(x=FAKE, idx=FAKE, rank=NULL, T=64, H=512, k=2, E=8, e0=0, El=8, R=1, tm=64,
+             xp=FAKE, cnt=FAKE, off=FAKE, rs=FAKE, inv=FAKE, tiles=FAKE, nt=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return L.moe_permute(a["x"], a["idx"], a["rank"], a["T"], a["H"], a["k"], a["E"], a["e0"], a["El"],
+                         a["R"], a["tm"], a["xp"], a["cnt"], a["off"], a["rs"], a["inv"], a["tiles"],
+                         a["nt"], a["ws"], a["wsb"], NULL)
+
+
+def test_permute_validation(L):
+    assert permute_call(L, e0=4, El=8) == INVALID          # local range beyond E
+    assert permute_call(L, El=0) == INVALID
+    assert permute_call(L, k=9) == INVALID                 # k > E
+    assert permute_call(L, tm=48) == UNSUPPORTED           # tile size not implemented
+    assert permute_call(L, H=500) == UNSUPPORTED           # H % 8
+    assert permute_call(L, R=65) == UNSUPPORTED            # too many ranks
+    assert permute_call(L, xp=NULL) == INVALID
+    assert permute_call(L, ws=ctypes.c_void_p(16 * 1024 + 8)) == INVALID
+    need = ffi.permute_workspace_bytes(64, 2, 8, 1)
+    assert permute_call(L, wsb=need - 1) == WORKSPACE
+    assert permute_call(L, T=0) == OK
+
+
+def ffn_call(L, **over):
+    a = dict(xp=FAKE, cnt=FAKE, off=FAKE, tiles=FAKE, nt=FAKE, w0=FAKE, w0u=FAKE, w1=FAKE, El=8, H=512,
+             F=1024, act=1, tm=64, Rcap=1000, tcap=20, ab=FAKE, y=FAKE)
+    a.update(over)
+    return L.moe_grouped_ffn(a["xp"], a["cnt"], a["off"], a["tiles"], a["nt"], a["w0"], a["w0u"], a["w1"],
+                             a["El"], a["H"], a["F"], a["act"], a["tm"], a["Rcap"], a["tcap"], a["ab"], a["y"],
+                             NULL)
+
+
+def test_grouped_ffn_validation(L):
+    assert ffn_call(L, act=0) == INVALID              # GELU with an up matrix
+    assert ffn_call(L, w0u=NULL) == INVALID           # SwiGLU without one
+    assert ffn_call(L, act=7) == INVALID
+    assert ffn_call(L, H=576) == UNSUPPORTED          # H % 128
+    assert ffn_call(L, F=1000) == UNSUPPORTED
+    assert ffn_call(L, tm=8) == UNSUPPORTED
+    assert ffn_call(L, y=NULL) == INVALID
+    assert ffn_call(L, Rcap=0) == OK                  # no rows: nothing launched
+
+
+def test_combine_validation(L):
+    assert L.moe_combine(FAKE, FAKE, FAKE, 10, 0, 512, 100, FAKE, NULL) == INVALID
+    assert L.moe_combine(FAKE, FAKE, FAKE, 10, 2, 510, 100, FAKE, NULL) == UNSUPPORTED
+    assert L.moe_combine(NULL, FAKE, FAKE, 10, 2, 512, 100, FAKE, NULL) == INVALID
+    assert L.moe_combine(NULL, NULL, NULL, 0, 2, 512, 0, NULL, NULL) == OK
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ffi, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ffi, "_lib", None)
+    with pytest.raises(ImportError):
+        ffi.lib()
