@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of an MoE layer (route -> permute -> grouped FFN -> combine).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--cpu-seconds S]
+
+A step is one pass of the whole layer over one batch of synthetic tokens whose
+inputs (tokens, router logits, source ranks, expert weights) are already
+resident in HBM.  W untimed steps, then K steps timed with HIP events on the
+stream the library launches on; per-call durations come from event pairs
+recorded around each of the four calls inside the same timed region.
+
+Prints ONE JSON line: throughput in TFLOP/s (algorithmic: 2*R*H*F per GEMM
+matrix, R = routed (token, local expert) rows, padding excluded), tokens/s,
+the fraction of the bf16 MFMA peak, a roofline entry for the dominant call
+(the grouped FFN: layer0 GEMM + fused activation + layer1 GEMM) and the CPU
+oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+
+WORKLOAD_NAMES = {
+    "tiny": "tiny MoE layer (256 tokens, hidden 512, FFN 1024, 8 experts top-2, GELU)",
+    "mixtral": "Mixtral-shaped MoE layer, one GPU's share (4096 tokens, hidden 4096, FFN 14336, "
+               "8 experts top-2, SwiGLU)",
+    "fine_grained": "fine-grained MoE layer (8192 tokens, hidden 2048, FFN 1408, 64 experts top-6, "
+                    "SwiGLU, Zipf(1.1)-biased router)",
+    "ep_share": "expert-parallel share (16384 tokens from 8 source ranks, 8 local of 64 experts, "
+                "top-8, hidden 4096, FFN 2048, SwiGLU)",
+    "decode": "decode-sized MoE layer (64 tokens, hidden 7168, FFN 2048, 256 experts top-8, SwiGLU)",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral", choices=list(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle sample budget in seconds (0 disables the CPU baseline)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, d, seconds):
+    """The oracle, as it stands, on a bounded sample of the workload's tokens (rank 0, host cores)."""
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+
+    from mixture_experts_layer_moe_amd import workloads as W
+    logits = d["logits"].cpu().numpy()
+    xs = d["x"]
+    order = np.random.default_rng(0).permutation(cfg.T)
+    cache = {}
+
+    def weights(le):
+        return cache[le]   # staged before the timer starts (below)
+
+    done, rows, elapsed = 0, 0, 0.0
+    for t in order[:64]:
+        t = int(t)
+        idx_t, _ = O.route_topk(logits[t:t + 1], cfg.k)
+        # input staging (untimed): this token's row and its local experts' weights on the host
+        for e in idx_t.ravel():
+            le = int(e) - cfg.expert_begin
+            if 0 <= le < cfg.n_local and le not in cache:
+                cache[le] = tuple(None if w is None else w[le].to("cpu", torch.float32).numpy()
+                                  for w in (d["w0"], d["w0_up"], d["w1"]))
+        x_t = xs[t].to("cpu", torch.float64).numpy()[None, :]
+        t0 = time.perf_counter()
+        O.moe_layer(x_t, logits[t:t + 1], cfg.k, weights, cfg.act,
+                    expert_begin=cfg.expert_begin, E_loc=cfg.n_local)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        rows += int(((idx_t >= cfg.expert_begin) & (idx_t < cfg.expert_begin + cfg.n_local)).sum())
+        if len(cache) > 16:   # bound host memory: keep the weights of at most 16 experts
+            cache.clear()
+        if elapsed >= seconds:
+            break
+    flop = W.flops(cfg, rows)
+    return {
+        "value": flop / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "tokens_per_s": done / elapsed,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} tokens of the workload ({rows} routed rows), float64 per-token loop, "
+                  f"{elapsed:.1f} s on {platform.processor() or platform.machine()}",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not "
+              "part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+    from mixture_experts_layer_moe_amd import workloads as W
+    from mixture_experts_layer_moe_amd.layer import MoELayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.workload]
+    d = W.make_inputs(cfg, dev)
+    layer = MoELayer.from_inputs(cfg, d)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.run()
+    torch.cuda.synchronize()
+
+    calls = [layer.route, layer.permute, layer.ffn, layer.combine]
+    names = ["route", "permute", "grouped_ffn", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        for i, c in enumerate(calls):
+            ev[s][i].record(stream)
+            c()
+        ev[s][len(calls)].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+
+    ms_step = start.elapsed_time(end) / args.steps
+    per_call = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                for i, n in enumerate(names)}
+
+    # algorithmic work of this batch
+    R = int(layer.perm.expert_counts.sum().item())
+    inv = layer.perm.inv_perm
+    T_hit = int((inv >= 0).any(dim=1).sum().item())
+    flop = W.flops(cfg, R)
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    ffn_tflops = flop / (per_call["grouped_ffn"] * 1e-3) / 1e12
+    permute_bytes = T_hit * cfg.H * 2 + R * cfg.H * 2
+    combine_bytes = R * cfg.H * 4 + cfg.T * cfg.H * 4
+
+    result = {
+        "metric": "MoE-layer TFLOP/s and tokens/s on 1 MI355X; % of bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": cfg.T, "hidden": cfg.H,
+                   "ffn": cfg.F, "experts": cfg.E, "local_experts": cfg.n_local, "top_k": cfg.k,
+                   "activation": cfg.act, "tile_m": layer.tile_m, "routed_rows": R},
+        "tokens_per_s": round(cfg.T / (ms_step * 1e-3), 1),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "per_call_ms": {n: round(v, 5) for n, v in per_call.items()},
+        "permute_GBps": round(permute_bytes / (per_call["permute"] * 1e-3) / 1e9, 1),
+        "combine_GBps": round(combine_bytes / (per_call["combine"] * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "moe_grouped_ffn (layer0 grouped GEMM + fused activation, layer1 grouped GEMM)",
+            "bound": "mfma",
+            "achieved": round(ffn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

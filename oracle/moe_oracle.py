@@ -246,3 +246,33 @@ def moe_layer(x: np.ndarray, logits: np.ndarray, k: int, weights, act: str,
             w0, w0u, w1 = get(le)
             out[i] += float(w[t, j]) * expert_ffn(x[t], w0, w0u, w1, act)
     return out
+
+
+def moe_layer_expert_major(x: np.ndarray, k: int, weights, act: str, route,
+                           tokens: Sequence[int], expert_begin: int = 0,
+                           E_loc: Optional[int] = None) -> np.ndarray:
+    """The same sum as moe_layer, visiting experts in the outer loop.
+
+    For large layers only a few token rows are checked, and each local
+    expert's weights are fetched once (weights(le) is called at most once per
+    expert, and only for experts some listed token selected).  route is the
+    (idx, w) pair of route_topk.  Row i of the result is token tokens[i].
+    """
+    x = np.asarray(x)
+    idx, w = route
+    T, _ = idx.shape
+    if E_loc is None:
+        E_loc = int(idx.max()) + 1 - expert_begin
+    get = weights if callable(weights) else weights.__getitem__
+    users = {}
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            le = int(idx[t, j]) - expert_begin
+            if 0 <= le < E_loc:
+                users.setdefault(le, []).append((i, t, j))
+    out = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)
+    for le in sorted(users):
+        w0, w0u, w1 = get(le)
+        for i, t, j in users[le]:
+            out[i] += float(w[t, j]) * expert_ffn(x[t], w0, w0u, w1, act)
+    return out

@@ -27,8 +27,16 @@ MUTANTS = [
      [("test_topk1_is_argmax_with_ties", {}), ("test_topk_matches_bruteforce", {"E": 5})]),
     ("gate not renormalised", "denom = math.fsum(z)", "denom = math.fsum(math.exp(v - top) for v in row)",
      [("test_gate_weights_sum_to_one_and_ratios", {})]),
-    ("layer drops the gate weight", "out[i] += float(w[t, j]) * expert_ffn", "out[i] += expert_ffn",
+    ("layer drops the gate weight", "w0, w0u, w1 = get(le)\n            out[i] += float(w[t, j]) * expert_ffn",
+     "w0, w0u, w1 = get(le)\n            out[i] += expert_ffn",
      [("test_layer_matches_dense_mixture", {"act": "swiglu", "renorm": True, "E": 4, "k": 2})]),
+    ("expert-major layer drops the gate weight",
+     "for i, t, j in users[le]:\n            out[i] += float(w[t, j]) * expert_ffn",
+     "for i, t, j in users[le]:\n            out[i] += expert_ffn",
+     [("test_expert_major_layer_matches_dense_mixture", {"act": "gelu"})]),
+    ("expert-major layer ignores expert_begin", "le = int(idx[t, j]) - expert_begin\n            if 0 <= le < E_loc:\n                users",
+     "le = int(idx[t, j])\n            if 0 <= le < E_loc:\n                users",
+     [("test_expert_major_layer_matches_dense_mixture", {"act": "swiglu"})]),
     ("combine drops the gate weight", "out[t] += float(topk_w[t, j]) * np.asarray", "out[t] += np.asarray",
      [("test_combine_and_permute_reassemble_the_layer", {})]),
     ("transposed layer-1 weight", "return np.asarray(w1, dtype=np.float64) @ a",
@@ -42,7 +50,8 @@ MUTANTS = [
     ("tile priority from the first row", "last = offsets[le] + min(counts[le], (m + 1) * tile_m) - 1",
      "last = offsets[le] + m * tile_m",
      [("test_permute_invariants", {"T": 500, "k": 8, "E": 64, "e0": 8, "El": 8, "R": 8, "tm": 64})]),
-    ("local range ignores expert_begin", "le = int(idx[t, j]) - expert_begin", "le = int(idx[t, j])",
+    ("local range ignores expert_begin", "le = int(idx[t, j]) - expert_begin\n            if not 0",
+     "le = int(idx[t, j])\n            if not 0",
      [("test_rank_partition_invariance", {})]),
 ]
 

@@ -314,3 +314,26 @@ def test_activation_closed_forms():
     assert O.gelu(np.array([0.0]))[0] == 0.0
     # GELU(x) = x * Phi(x): compare with the normal CDF from scipy
     assert np.allclose(O.gelu(z), z * scipy.special.ndtr(z), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_expert_major_layer_matches_dense_mixture(act):
+    # The expert-major visiting order (used for sampled checks of big layers) gives the same rows
+    # as the fp64 dense mixture, for any token subset and local expert range.
+    rng = np.random.default_rng(11)
+    T, H, F, E, k = 12, 16, 24, 6, 3
+    X = rng.standard_normal((T, H))
+    L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    ws = rand_weights(rng, E, H, F, act)
+    calls = []
+
+    def get(le):
+        calls.append(le)
+        return ws[1 + le]
+
+    tokens = [7, 0, 11, 3, 3]
+    route = O.route_topk(L, k)
+    out = O.moe_layer_expert_major(X, k, get, act, route, tokens, expert_begin=1, E_loc=4)
+    ref = dense_mixture(X, L, k, ws[1:5], act, expert_begin=1, E_loc=4)[tokens]
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-12)
+    assert len(calls) == len(set(calls))          # each expert's weights fetched at most once
