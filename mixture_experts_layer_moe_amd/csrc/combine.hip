@@ -7,46 +7,72 @@
 //   out[t, :] = sum_{j = 0..k-1, inv_perm[t, j] >= 0} topk_w[t, j] * y_perm[inv_perm[t, j], :]
 //
 // HBM-bound: reads each routed row once (fp32), writes each token row once.
-// One block per group of tokens; each thread owns 16-byte (float4) column
-// chunks and sums the k slots in slot order in registers, so the result is
-// deterministic and needs no atomics.
+// A block owns one token (blockIdx.x, block-uniform, so its k row indices and weights are
+// scalar loads) and a span of kCols float4 columns; each thread issues the
+// loads of all k slots before the first add, then sums in slot order in
+// registers, so the result is deterministic and needs no atomics.  Rows are
+// streamed once, so loads and stores bypass the caches' retention
+// (nontemporal).
 #include "common.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const floatx4* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ inv_perm,
-                                                      const float* __restrict__ topk_w, int64_t T,
-                                                      int k, int H4, int64_t R_cap,
-                                                      floatx4* __restrict__ out, int tokens_per_block) {
-  // Threads split into tokens_per_block groups; group g handles token t.
-  const int group_size = blockDim.x / tokens_per_block;
-  const int g = threadIdx.x / group_size, gt = threadIdx.x % group_size;
-  const int64_t t = (int64_t)blockIdx.x * tokens_per_block + g;
-  if (t >= T) return;
-  int rows[32];
-  float w[32];
+constexpr int kThreads = 256;
+constexpr int kVec = 2;                      // float4 per thread
+constexpr int kCols = kThreads * kVec;       // float4 columns per block
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const floatx4* __restrict__ y_perm,
+                                                           const int32_t* __restrict__ inv_perm,
+                                                           const float* __restrict__ topk_w, int k_rt,
+                                                           int H4, int64_t R_cap,
+                                                           floatx4* __restrict__ out) {
+  const int kk = K > 0 ? K : k_rt;
+  const int64_t t = blockIdx.x;
+  const int c0 = blockIdx.y * kCols + threadIdx.x;
+  floatx4 acc[kVec];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    rows[j] = -1;
-    w[j] = 0.f;
-    if (j < k) {
-      const int p = inv_perm[t * k + j];
+  for (int v = 0; v < kVec; ++v) acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (K > 0) {
+    int rows[K > 0 ? K : 1];
+    float w[K > 0 ? K : 1];
+    floatx4 y[K > 0 ? K : 1][kVec];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int p = inv_perm[t * K + j];
       rows[j] = (p >= 0 && p < R_cap) ? p : -1;
-      w[j] = topk_w[t * k + j];
+      w[j] = topk_w[t * K + j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const int c = c0 + v * kThreads;
+        y[j][v] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (rows[j] >= 0 && c < H4) y[j][v] = __builtin_nontemporal_load(y_perm + (int64_t)rows[j] * H4 + c);
+      }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (rows[j] >= 0)
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) acc[v] += w[j] * y[j][v];
+  } else {
+    for (int j = 0; j < kk; ++j) {
+      const int p = inv_perm[t * kk + j];
+      if (p < 0 || p >= R_cap) continue;
+      const float w = topk_w[t * kk + j];
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const int c = c0 + v * kThreads;
+        if (c < H4) acc[v] += w * y_perm[(int64_t)p * H4 + c];
+      }
     }
   }
-  floatx4* o = out + t * H4;
-  for (int c = gt; c < H4; c += group_size) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (rows[j] < 0) continue;
-      const floatx4 y = y_perm[(int64_t)rows[j] * H4 + c];
-      acc += w[j] * y;
-    }
-    o[c] = acc;
+  for (int v = 0; v < kVec; ++v) {
+    const int c = c0 + v * kThreads;
+    if (c < H4) __builtin_nontemporal_store(acc[v], out + t * H4 + c);
   }
 }
 
@@ -55,13 +81,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const floatx4* __restrict_
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T,
                           int k, int H, int64_t R_cap, float* out, hipStream_t s) {
   const int H4 = H / 4;
-  // Enough threads per token to cover a row in a few passes; small rows share a block.
-  int tpb = 1;  // tokens per block; each token keeps a multiple of 64 threads
-  while (tpb < 4 && 256 / (tpb * 2) >= H4) tpb *= 2;
-  const int64_t blocks = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     reinterpret_cast<const floatx4*>(y_perm), inv_perm, topk_w, T, k, H4, R_cap,
-                     reinterpret_cast<floatx4*>(out), tpb);
+  const dim3 grid((unsigned)T, (unsigned)((H4 + kCols - 1) / kCols));
+  const floatx4* y = reinterpret_cast<const floatx4*>(y_perm);
+  floatx4* o = reinterpret_cast<floatx4*>(out);
+#define MOE_COMBINE_CASE(KV) \
+  case KV: hipLaunchKernelGGL(combine_kernel<KV>, grid, dim3(kThreads), 0, s, y, inv_perm, topk_w, k, H4, R_cap, o); break;
+  switch (k) {
+    MOE_COMBINE_CASE(1)
+    MOE_COMBINE_CASE(2)
+    MOE_COMBINE_CASE(4)
+    MOE_COMBINE_CASE(6)
+    MOE_COMBINE_CASE(8)
+    default: hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(kThreads), 0, s, y, inv_perm, topk_w, k, H4, R_cap, o);
+  }
+#undef MOE_COMBINE_CASE
   return hipGetLastError();
 }
 

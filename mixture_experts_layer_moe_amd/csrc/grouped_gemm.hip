@@ -3,10 +3,12 @@
 // "Comet: Fine-grained Computation-communication Overlapping for
 // Mixture-of-Experts":
 //   - section 3.1.2: one GroupGEMM computes all experts of this rank over
-//     tile-aligned sub-tensors, tiles holding local tokens first;
+//     tile-aligned sub-tensors, tiles holding local tokens first; layer1 runs
+//     column block by column block so the reduce can start after the first
+//     column blocks;
 //   - section 3.1.1: layer0 is decomposed along M (token rows are
 //     independent), layer1 along N (the top-k reduce couples rows across
-//     experts, so output columns are produced block by block);
+//     experts);
 //   - section 4: the MoE GEMMs avoid re-reading row indices from global
 //     memory on every K iteration (here the rows are already contiguous, so
 //     a tile needs only its first row and its expert).
@@ -14,25 +16,37 @@
 // local experts without relaunches.
 //
 // Design (MI355X / CDNA4):
-//   * Persistent grid, one workgroup per CU (or more for small tiles); the
-//     work-item list is (tile, column block) pairs, read from the device tile
-//     list, so the host never needs the per-expert row counts.
+//   * Persistent grid of one workgroup per CU; the work items are (row tile,
+//     column block) pairs read from the device tile list, so the host never
+//     needs the per-expert row counts.
 //   * Workgroup ids are remapped so that each XCD (workgroups are dispatched
-//     round-robin over the 8 XCDs) processes a contiguous run of work items;
-//     items that run together share operand panels through that XCD's L2.
+//     round-robin over the 8 XCDs) runs a contiguous run of work items: the
+//     items an XCD runs together form a small rectangle of row tiles x
+//     column blocks whose operand panels are shared through that XCD's L2.
 //   * Layer0 order: groups of kGroupM consecutive tiles of the tile list;
 //     inside a group, column block major then tile.  Layer1 order: column
-//     block major over the whole tile list (N-decomposition).
+//     groups of kGroupN blocks (N-decomposition: a column group is finished
+//     for all tiles before the next starts); inside a group, tile major.
 //   * Operands are staged HBM -> LDS with global_load_lds_dwordx4 (16 bytes
-//     per lane straight into LDS, no VGPR round trip), double buffered, BK=64.
-//     Each LDS row holds 64 bf16 (128 B) of one operand row; the 16-byte
-//     chunk index is XOR-swizzled with (row & 7) so the MFMA fragment reads
-//     (16 rows x 16 bytes per 16 lanes) are bank-conflict free.
-//   * MFMA v_mfma_f32_16x16x32_bf16 with operand roles swapped: the weight
-//     tile feeds the A side (rows = output columns n) and the token tile the
-//     B side (columns = token rows m).  Each lane then holds 4 consecutive
-//     output columns of one row, so the epilogue stores 8 B (bf16) or 16 B
-//     (fp32) vectors.
+//     per lane straight into LDS, no VGPR round trip) in a ring of STAGES
+//     buffers, BK = 64.  Each LDS row holds 64 bf16 (128 B) of one operand
+//     row; the 16-byte chunk index is XOR-swizzled with
+//     (row & 7) ^ ((row >> 3) & 1), so that the fragment reads (consecutive
+//     lanes read consecutive rows at one chunk) hit distinct banks both for
+//     8 lanes within 128 B and for 16 lanes within 256 B.
+//   * The stage boundary is software-pipelined: the wait for the next stage,
+//     the barrier and the next stage's first fragment reads are issued
+//     before the last MFMAs of the current stage, which keep the matrix
+//     cores busy meanwhile.
+//   * Big tiles (tile_m >= 128): 4 waves (one per SIMD), each owning a
+//     128 x 128 (or 64 x 128) accumulator tile of v_mfma_f32_32x32x16_bf16,
+//     which keeps LDS traffic per flop at half of the LDS bandwidth.  Small
+//     tiles (tile_m <= 64, weight-streaming shapes): 8 waves of
+//     v_mfma_f32_16x16x32_bf16.
+//   * Operand roles are swapped: the weight tile feeds the MFMA A side
+//     (rows = output columns n) and the token tile the B side (columns =
+//     token rows m).  Each lane then holds 4 consecutive output columns of
+//     one row, so the epilogue stores 8 B (bf16) or 16 B (fp32) vectors.
 //   * Epilogue: SwiGLU silu(g) * u, or exact-erf GELU, in fp32, rounded to
 //     bf16 (nearest even) for layer0; plain fp32 for layer1.  Rows past the
 //     expert's real count are never stored.
@@ -43,47 +57,303 @@ namespace {
 
 constexpr int BK = 64;          // K per stage (one 128-byte LDS row per operand row)
 constexpr int kGroupM = 8;      // layer0: tiles per rasterisation group
+constexpr int kGroupN = 4;      // layer1: column blocks per column group
 constexpr int kXcds = 8;
+constexpr int MOE_ACT_SWIGLU_I = 1;  // moe_act value of SwiGLU
 
 enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_F32 = 2 };
+enum Order { ORDER_M = 0, ORDER_N = 1 };
 
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each, far below the
+// bf16 rounding that follows).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 __device__ __forceinline__ float gelu_f(float h) { return 0.5f * h * (1.0f + erff(h * 0.70710678118654752f)); }
 
+// s_waitcnt with vmcnt = n (0..63) and the other counters left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Raw buffer resource over [base, base + bytes): out-of-range reads return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // Load ROWS operand rows x 64 bf16 (row stride ld elements) into a swizzled
-// LDS tile with direct-to-LDS loads: one wave instruction moves 8 rows.
+// LDS tile with direct-to-LDS loads: one wave instruction moves 8 rows; lane
+// L writes physical chunk L % 8 of row L / 8 and fetches the logical chunk
+// that belongs there.
 template <int ROWS, int NWAVES>
 __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ g, int64_t ld, char* lds,
                                            int wave, int lane) {
+  static_assert(ROWS % (8 * NWAVES) == 0, "rows per wave");
   const int r_in = lane >> 3;                  // row within the 8-row group
-  const int chunk = (lane & 7) ^ r_in;         // logical 16-byte chunk this lane fetches
-  const uint16_t* src = g + (int64_t)r_in * ld + chunk * 8;
 #pragma unroll
-  for (int grp = wave; grp < ROWS / 8; grp += NWAVES) {
-    __builtin_amdgcn_global_load_lds(src + (int64_t)grp * 8 * ld, (lds_void*)(lds + grp * 1024), 16, 0, 0);
+  for (int q = 0; q < ROWS / (8 * NWAVES); ++q) {
+    const int grp = q * NWAVES + wave;
+    const int chunk = (lane & 7) ^ swz(grp * 8 + r_in);
+    const uint16_t* src = g + (int64_t)(grp * 8 + r_in) * ld + chunk * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + grp * 1024), 16, 0, 0);
   }
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ (row & 7)) << 4));
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz(row)) << 4));
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, bool NMAJOR>
-__global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(
+// s_waitcnt lgkmcnt(0), other counters left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Wait until at most n * per direct-to-LDS loads of this wave are in flight (n small, runtime).
+template <int per, int max_n>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (max_n >= 2 && n >= 2) wait_vmcnt<(max_n >= 2 ? 2 * per : 0)>();
+  else if (max_n >= 1 && n >= 1) wait_vmcnt<(max_n >= 1 ? per : 0)>();
+  else wait_vmcnt<0>();
+}
+
+// Work item -> (tile index, column block).
+template <int ORDER>
+__device__ __forceinline__ void item_coords(int64_t item, int nt, int nbn, int& tile_i, int& nb) {
+  if (ORDER == ORDER_N) {
+    const int64_t per_group = (int64_t)nt * kGroupN;
+    const int g = (int)(item / per_group);
+    const int rem = (int)(item % per_group);
+    const int gsize = (nbn - g * kGroupN) < kGroupN ? (nbn - g * kGroupN) : kGroupN;
+    tile_i = rem / gsize;
+    nb = g * kGroupN + rem % gsize;
+  } else {
+    const int64_t per_group = (int64_t)kGroupM * nbn;
+    const int grp = (int)(item / per_group);
+    const int rem = (int)(item % per_group);
+    const int gsize = (nt - grp * kGroupM) < kGroupM ? (nt - grp * kGroupM) : kGroupM;
+    nb = rem / gsize;
+    tile_i = grp * kGroupM + rem % gsize;
+  }
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int G) { return (bid % kXcds) * (G / kXcds) + bid / kXcds; }
+
+// Epilogue for 4 consecutive output columns of one row.
+template <int EPI>
+__device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const float* g, const float* u) {
+  if (EPI == EPI_F32) {
+    *reinterpret_cast<floatx4*>(static_cast<float*>(C) + row * N + n) = floatx4{g[0], g[1], g[2], g[3]};
+  } else {
+    uint16_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = (EPI == EPI_SWIGLU) ? silu_f(g[q]) * u[q] : gelu_f(g[q]);
+      h[q] = f2bf_bits(a);
+    }
+    const uint2 packed = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) = packed;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Big-tile kernel: 4 waves (2 x 2), v_mfma_f32_32x32x16_bf16, STAGES-deep LDS ring.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const uint16_t* __restrict__ A,    // [R_cap, K] bf16 (x_perm or act)
     const uint16_t* __restrict__ B0,   // [E_loc, N, K] bf16
     const uint16_t* __restrict__ B1,   // [E_loc, N, K] bf16 (DUAL) or null
     int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
     int64_t R_cap, int E_loc, void* __restrict__ C) {
-  constexpr int NWAVES = WM * WN;
+  constexpr int NWAVES = 4, WN = 2;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BROWS = NMAT * BN;               // weight rows staged per stage
   constexpr int A_BYTES = BM * 128, B_BYTES = BROWS * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int WT_M = BM / WM, WT_N = BN / WN;  // wave tile (per matrix)
+  constexpr int WT_M = BM / 2, WT_N = BN / WN;
+  constexpr int TM = WT_M / 32, TN = WT_N / 32;
+  constexpr int LOADS = (BM + BROWS) / 8 / NWAVES;  // direct-to-LDS loads per wave per stage
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  static_assert(STAGES >= 2 && STAGES <= 3 && (STAGES - 1) * LOADS < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int G = gridDim.x;
+  const int vid = xcd_remap(blockIdx.x, G);
+  int nt = *num_tiles;
+  if (nt > tiles_cap) nt = (int)tiles_cap;
+  const int nbn = N / BN;
+  const int64_t total = (int64_t)nt * nbn;
+  const int nk = K / BK;
+  const int64_t b_expert = (int64_t)N * K;
+  for (int64_t item = vid; item < total; item += G) {
+    int tile_i, nb;
+    item_coords<ORDER>(item, nt, nbn, tile_i, nb);
+    const int le = tiles[2 * tile_i];
+    const int row0 = tiles[2 * tile_i + 1];
+    if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) continue;  // block-uniform
+    int valid = counts[le] - (row0 - offsets[le]);
+    valid = valid < BM ? valid : BM;
+    const int n0 = nb * BN;
+    // Buffer resources based at this item's operand panels (ranges of a few MiB,
+    // out-of-range reads return zeros).  A and B share the row stride K, so one
+    // per-lane byte offset serves every direct-to-LDS load of this wave:
+    // row (q * NWAVES + wave) * 8 + lane / 8, logical chunk swizzled for that row.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
+    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
+    const __amdgpu_buffer_rsrc_t rb1 = DUAL ? make_rsrc(B1 + le * b_expert + (int64_t)n0 * K, BN * K * 2) : rb0;
+    const int r_in = lane >> 3;
+    const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
+    floatx16 acc[NMAT][TN][TM];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][j][i][v] = 0.f;
+    auto issue = [&](int stage, int k0) {
+      char* s = smem + stage * STAGE;
+#pragma unroll
+      for (int q = 0; q < BM / (8 * NWAVES); ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(s + (q * NWAVES + wave) * 1024), 16, voff,
+                                                 (q * 8 * NWAVES * K + k0) * 2, 0, 0);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int q = 0; q < BN / (8 * NWAVES); ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? rb1 : rb0,
+                                                   (lds_void*)(s + A_BYTES + m * BN * 128 + (q * NWAVES + wave) * 1024),
+                                                   16, voff, (q * 8 * NWAVES * K + k0) * 2, 0, 0);
+    };
+    struct Frags {
+      bf16x8 a[TM];
+      bf16x8 b[NMAT][TN];
+    };
+    auto read_frags = [&](int stage, int ks) {
+      const char* sA = smem + stage * STAGE;
+      const char* sB = sA + A_BYTES;
+      const int chunk = ks * 2 + (lane >> 5);
+      Frags f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) f.a[i] = lds_frag(sA, wm * WT_M + i * 32 + (lane & 31), chunk);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) f.b[m][j] = lds_frag(sB, m * BN + wn * WT_N + j * 32 + (lane & 31), chunk);
+      return f;
+    };
+// MFMAs number [first, first + count) of one 16-wide K step (order: matrix, column block, row block).
+#define MOE_MFMAS(F, FIRST, COUNT)                                                                        \
+  _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                                        \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                          \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                        \
+    const int idx_ = (m * TN + j) * TM + i;                                                               \
+    if (idx_ >= (FIRST) && idx_ < (FIRST) + (COUNT))                                                      \
+      acc[m][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((F).b[m][j], (F).a[i], acc[m][j][i], 0, 0, 0); \
+  }
+    constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
+    constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
+
+    // Prologue: fill every buffer of the ring, then wait for stage 0.
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s, s * BK);
+    wait_stages<LOADS, STAGES - 1>(nk - 1 < STAGES - 1 ? nk - 1 : STAGES - 1);
+    __syncthreads();
+    Frags cur = read_frags(0, 0);
+    // K steps of one stage but the last: the next step's fragments are read
+    // while this step's MFMAs issue.
+#define MOE_INNER_STEPS(BUF)                                       \
+  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {     \
+    const Frags nxt = read_frags((BUF), ks + 1);                   \
+    MOE_MFMAS(cur, 0, NMFMA)                                       \
+    _Pragma("unroll") for (int g = 0; g < NREAD; ++g) {            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           \
+    }                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0); \
+    __builtin_amdgcn_sched_barrier(0);                             \
+    cur = nxt;                                                     \
+  }
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const int buf = kt % STAGES;
+      MOE_INNER_STEPS(buf)
+      // Last K step of the stage: half of its MFMAs keep the matrix cores busy
+      // across the stage boundary.
+      MOE_MFMAS(cur, 0, NMFMA / 2)
+      __builtin_amdgcn_sched_barrier(0);
+      // Stage kt+1 has landed once only the stages issued after it are in flight.
+      const int newer = (nk - 2 - kt) < (STAGES - 2) ? (nk - 2 - kt) : (STAGES - 2);
+      wait_stages<LOADS, STAGES - 2>(newer);
+      wait_lgkm0();     // this wave's reads of stage kt are complete
+      __syncthreads();  // stage kt+1 visible to all; buffer kt is free for stage kt+STAGES
+      __builtin_amdgcn_sched_barrier(0);
+      const Frags nxt = read_frags((kt + 1) % STAGES, 0);
+      if (kt + STAGES < nk) issue(buf, (kt + STAGES) * BK);
+      MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
+      __builtin_amdgcn_sched_barrier(0);
+      cur = nxt;
+    }
+    {  // the last stage
+      const int buf = (nk - 1) % STAGES;
+      MOE_INNER_STEPS(buf)
+      MOE_MFMAS(cur, 0, NMFMA)
+    }
+#undef MOE_INNER_STEPS
+#undef MOE_MFMAS
+
+    // Epilogue: lane holds, for token row m = lane % 32 of each 32-row block,
+    // output columns q*8 + (lane/32)*4 + 0..3 (q = 0..3) of each 32-column block.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * WT_M + i * 32 + (lane & 31);
+      if (m >= valid) continue;
+      const int64_t row = (int64_t)row0 + m;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
+          float g[4], u[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            g[r] = acc[0][j][i][q * 4 + r];
+            u[r] = acc[NMAT - 1][j][i][q * 4 + r];
+          }
+          store4<EPI>(C, row, N, n, g, u);
+        }
+    }
+    wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
+    __syncthreads();  // the next item's first stages overwrite LDS
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small-tile kernel (tile_m <= 64): WM x WN waves of v_mfma_f32_16x16x32_bf16,
+// double-buffered LDS.  These shapes stream weights from HBM.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, int ORDER>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+    int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
+    int64_t R_cap, int E_loc, void* __restrict__ C) {
+  constexpr int NWAVES = WM * WN;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BROWS = NMAT * BN;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BROWS * 128;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int WT_M = BM / WM, WT_N = BN / WN;
   constexpr int TM = WT_M / 16, TN = WT_N / 16;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(BM % 8 == 0 && BROWS % 8 == 0, "rows per stage");
@@ -93,7 +363,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int G = gridDim.x;
-  const int vid = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  const int vid = xcd_remap(blockIdx.x, G);
 
   int nt = *num_tiles;
   if (nt > tiles_cap) nt = (int)tiles_cap;
@@ -102,19 +372,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(
   const int nk = K / BK;
   const int64_t b_expert = (int64_t)N * K;
 
+  // rows per stage may not be a multiple of 8 * NWAVES: guard per 8-row group
+  auto stage_any = [&](const uint16_t* g, int rows, char* lds) {
+    const int r_in = lane >> 3;
+    for (int grp = wave; grp < rows / 8; grp += NWAVES) {
+      const int chunk = (lane & 7) ^ swz(grp * 8 + r_in);
+      __builtin_amdgcn_global_load_lds(g + (int64_t)(grp * 8 + r_in) * K + chunk * 8, (lds_void*)(lds + grp * 1024),
+                                       16, 0, 0);
+    }
+  };
+
   for (int64_t item = vid; item < total; item += G) {
     int tile_i, nb;
-    if (NMAJOR) {
-      nb = (int)(item / nt);
-      tile_i = (int)(item % nt);
-    } else {
-      const int64_t per_group = (int64_t)kGroupM * nbn;
-      const int grp = (int)(item / per_group);
-      const int64_t rem = item % per_group;
-      const int gsize = (nt - grp * kGroupM) < kGroupM ? (nt - grp * kGroupM) : kGroupM;
-      nb = (int)(rem / gsize);
-      tile_i = grp * kGroupM + (int)(rem % gsize);
-    }
+    item_coords<ORDER>(item, nt, nbn, tile_i, nb);
     const int le = tiles[2 * tile_i];
     const int row0 = tiles[2 * tile_i + 1];
     if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) continue;  // block-uniform
@@ -136,15 +406,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(
 
     auto issue = [&](int stage, int k0) {
       char* s = smem + stage * STAGE;
-      stage_rows<BM, NWAVES>(a_g + k0, K, s, wave, lane);
-      stage_rows<BN, NWAVES>(b0_g + k0, K, s + A_BYTES, wave, lane);
-      if (DUAL) stage_rows<BN, NWAVES>(b1_g + k0, K, s + A_BYTES + BN * 128, wave, lane);
+      stage_any(a_g + k0, BM, s);
+      stage_any(b0_g + k0, BN, s + A_BYTES);
+      if (DUAL) stage_any(b1_g + k0, BN, s + A_BYTES + BN * 128);
     };
 
     issue(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads for stage kt have landed
-      __syncthreads();                // ... and everyone's; the other stage is free
+      wait_vmcnt<0>();
+      __syncthreads();
       if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
       const char* sA = smem + (kt & 1) * STAGE;
       const char* sB = sA + A_BYTES;
@@ -178,23 +448,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int n = n0 + wn * WT_N + i * 16 + 4 * (lane >> 4);
-        if (EPI == EPI_F32) {
-          *reinterpret_cast<floatx4*>(static_cast<float*>(C) + row * N + n) = acc[0][i][j];
-        } else {
-          uint16_t h[4];
+        float g[4], u[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float g = acc[0][i][j][q];
-            float a;
-            if (EPI == EPI_SWIGLU) a = silu_f(g) * acc[NMAT - 1][i][j][q];
-            else a = gelu_f(g);
-            h[q] = f2bf_bits(a);
-          }
-          const uint2 packed = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) = packed;
+        for (int r = 0; r < 4; ++r) {
+          g[r] = acc[0][i][j][r];
+          u[r] = acc[NMAT - 1][i][j][r];
         }
+        store4<EPI>(C, row, N, n, g, u);
       }
     }
+    wait_vmcnt<0>();
     __syncthreads();  // the next item's first stage overwrites LDS
   }
 }
@@ -211,42 +474,66 @@ int num_cus() {
   return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, bool NMAJOR>
-hipError_t launch_one(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int N, int K, const FfnArgs& a,
-                      void* C, hipStream_t s) {
-  const int64_t max_items = a.tiles_cap * (N / BN);
+// Persistent grid: one workgroup per CU (a multiple of the XCD count), fewer if there are fewer items.
+int64_t persistent_grid(int64_t max_items) {
   int64_t grid = num_cus();
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (max_items < grid) grid = (max_items + kXcds - 1) / kXcds * kXcds;
   if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, DUAL, EPI, NMAJOR>), dim3((unsigned)grid),
-                     dim3(WM * WN * 64), 0, s, A, B0, B1, N, K, a.counts, a.offsets, a.tiles, a.num_tiles,
-                     a.tiles_cap, a.R_cap, a.E_loc, C);
+  return grid;
+}
+
+template <typename Kern>
+hipError_t launch_persistent(Kern kern, int threads, int64_t max_items, const uint16_t* A, const uint16_t* B0,
+                             const uint16_t* B1, int N, int K, const FfnArgs& a, void* C, hipStream_t s) {
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items)), dim3(threads), 0, s, A, B0, B1, N, K,
+                     a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, C);
   return hipGetLastError();
 }
 
-// Per-tile_m kernel shapes: layer0 uses BN columns of each of gate and up.
-template <int BM, int WM, int WN, int BN0, int BN1, int WM1, int WN1>
-hipError_t launch_tm(const FfnArgs& a, hipStream_t s) {
+// tile_m >= 128: layer0 = BM x (BN0 gate + BN0 up) (GELU: BM x BN0), layer1 = BM x BN1
+// (BM x 128 when H is not a multiple of BN1).
+template <int BM, int BN0, int ST0, int BN1, int ST1>
+hipError_t launch_big(const FfnArgs& a, hipStream_t s) {
   hipError_t e;
-  if (a.act == 1) {
-    e = launch_one<BM, BN0, WM, WN, true, EPI_SWIGLU, false>(a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, s);
-  } else {
-    e = launch_one<BM, BN0, WM, WN, false, EPI_GELU, false>(a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, s);
-  }
+  if (a.act == MOE_ACT_SWIGLU_I)
+    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
+                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, s);
+  else
+    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
+                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, s);
   if (e != hipSuccess) return e;
-  return launch_one<BM, BN1, WM1, WN1, false, EPI_F32, true>(a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+  if (a.H % BN1 == 0)
+    return launch_persistent(gemm_mfma32_kernel<BM, BN1, false, EPI_F32, ORDER_N, ST1>, 256,
+                             a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+  return launch_persistent(gemm_mfma32_kernel<BM, 128, false, EPI_F32, ORDER_N, ST0>, 256, a.tiles_cap * (a.H / 128),
+                           a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+}
+
+// tile_m <= 64: weight-streaming shapes.
+template <int BM, int WM, int WN, int BN0, int BN1, int WM1, int WN1>
+hipError_t launch_small(const FfnArgs& a, hipStream_t s) {
+  hipError_t e;
+  if (a.act == MOE_ACT_SWIGLU_I)
+    e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, true, EPI_SWIGLU, ORDER_M>, WM * WN * 64,
+                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, s);
+  else
+    e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, false, EPI_GELU, ORDER_M>, WM * WN * 64,
+                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, s);
+  if (e != hipSuccess) return e;
+  return launch_persistent(gemm_mfma16_kernel<BM, BN1, WM1, WN1, false, EPI_F32, ORDER_N>, WM1 * WN1 * 64,
+                           a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
 }
 
 }  // namespace
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
   switch (a.tile_m) {
-    case 256: return launch_tm<256, 2, 4, 128, 128, 4, 2>(a, s);
-    case 128: return launch_tm<128, 2, 4, 128, 128, 2, 4>(a, s);
-    case 64: return launch_tm<64, 1, 8, 128, 128, 1, 8>(a, s);
-    case 32: return launch_tm<32, 1, 8, 128, 128, 1, 8>(a, s);
-    case 16: return launch_tm<16, 1, 8, 128, 128, 1, 8>(a, s);
+    case 256: return launch_big<256, 128, 2, 256, 2>(a, s);
+    case 128: return launch_big<128, 128, 3, 256, 3>(a, s);
+    case 64: return launch_small<64, 1, 8, 128, 128, 1, 8>(a, s);
+    case 32: return launch_small<32, 1, 8, 128, 128, 1, 8>(a, s);
+    case 16: return launch_small<16, 1, 8, 128, 128, 1, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -137,7 +137,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, con
 moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int32_t k,
                        int32_t H, int64_t R_cap, float* out, void* stream) {
   if (T < 0 || k < 1 || H < 1 || R_cap < 0) return MOE_ERR_INVALID_ARG;
-  if (H % 4 != 0 || k > 32) return MOE_ERR_UNSUPPORTED;
+  if (H % 4 != 0 || k > 32 || T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_perm || !inv_perm || !topk_w || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_perm) || !aligned16(inv_perm) || !aligned16(topk_w) || !aligned16(out))
