@@ -45,6 +45,7 @@ def assert_output_close(got: np.ndarray, ref: np.ndarray, what: str = "output"):
     max_err = float(err.max()) if err.size else 0.0
     denom = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref)) / denom if denom > 0 else float(np.linalg.norm(got))
+    print(f"[parity] {what}: max |err| {max_err:.3e}, rel-Frobenius {rel:.3e}", flush=True)
     assert max_err <= MAX_ABS_ERR, f"{what}: max |err| {max_err:.3e} > {MAX_ABS_ERR}"
     assert rel <= REL_FROB_ERR, f"{what}: relative Frobenius error {rel:.3e} > {REL_FROB_ERR}"
     return max_err, rel
