@@ -49,8 +49,9 @@ struct FfnArgs {
   int64_t R_cap, tiles_cap;
   uint16_t* act_buf;
   float* y_perm;
+  hipStream_t stream;
 };
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_grouped_ffn(const FfnArgs& a);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                           int64_t T, int k, int H, int64_t R_cap, float* out, hipStream_t s);

@@ -162,8 +162,174 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 }
 
 // ---------------------------------------------------------------------------
-// Big-tile kernel: 4 waves (2 x 2), v_mfma_f32_32x32x16_bf16, STAGES-deep LDS ring.
+// Big-tile path: 4 waves (2 x 2), v_mfma_f32_32x32x16_bf16, STAGES-deep LDS ring.
 // ---------------------------------------------------------------------------
+
+// One work item: rows [row0, row0 + BM) of expert le (valid of them real) times
+// output columns [n0, n0 + BN), reduction over [k_begin, k_begin + k_len).
+template <int BM, int BN, bool DUAL, int EPI, int STAGES>
+__device__ __forceinline__ void gemm_item(char* __restrict__ smem, const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+                                          int N, int K, int le, int row0, int valid, int n0, int k_begin, int k_len,
+                                          void* __restrict__ C, int wave, int lane) {
+  constexpr int NWAVES = 4, WN = 2;
+  constexpr int NMAT = DUAL ? 2 : 1;
+  constexpr int BROWS = NMAT * BN;               // weight rows staged per stage
+  constexpr int A_BYTES = BM * 128, B_BYTES = BROWS * 128;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int WT_M = BM / 2, WT_N = BN / WN;   // wave tile (per matrix)
+  constexpr int TM = WT_M / 32, TN = WT_N / 32;
+  constexpr int LOADS = (BM + BROWS) / 8 / NWAVES;  // direct-to-LDS loads per wave per stage
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  static_assert(STAGES >= 2 && STAGES <= 3 && (STAGES - 1) * LOADS < 64, "vmcnt range");
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = k_len / BK;
+  const int64_t b_expert = (int64_t)N * K;
+
+  // Buffer resources based at this item's operand panels (ranges of a few MiB,
+  // out-of-range reads return zeros).  A and B share the row stride K, so one
+  // per-lane byte offset serves every direct-to-LDS load of this wave:
+  // row (q * NWAVES + wave) * 8 + lane / 8, logical chunk swizzled for that row.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
+  const __amdgpu_buffer_rsrc_t rb1 = DUAL ? make_rsrc(B1 + le * b_expert + (int64_t)n0 * K, BN * K * 2) : rb0;
+  const int r_in = lane >> 3;
+  const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
+  floatx16 acc[NMAT][TN][TM];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][j][i][v] = 0.f;
+  auto issue = [&](int stage, int k0) {
+    char* s = smem + stage * STAGE;
+#pragma unroll
+    for (int q = 0; q < BM / (8 * NWAVES); ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(s + (q * NWAVES + wave) * 1024), 16, voff,
+                                               (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int q = 0; q < BN / (8 * NWAVES); ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? rb1 : rb0,
+                                                 (lds_void*)(s + A_BYTES + m * BN * 128 + (q * NWAVES + wave) * 1024),
+                                                 16, voff, (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
+  };
+  struct Frags {
+    bf16x8 a[TM];
+    bf16x8 b[NMAT][TN];
+  };
+  auto read_frags = [&](int stage, int ks) {
+    const char* sA = smem + stage * STAGE;
+    const char* sB = sA + A_BYTES;
+    const int chunk = ks * 2 + (lane >> 5);
+    Frags f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = lds_frag(sA, wm * WT_M + i * 32 + (lane & 31), chunk);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) f.b[m][j] = lds_frag(sB, m * BN + wn * WT_N + j * 32 + (lane & 31), chunk);
+    return f;
+  };
+// MFMAs number [first, first + count) of one 16-wide K step (order: matrix, column block, row block).
+#define MOE_MFMAS(F, FIRST, COUNT)                                                                        \
+  _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                                        \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                          \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                        \
+  const int idx_ = (m * TN + j) * TM + i;                                                               \
+  if (idx_ >= (FIRST) && idx_ < (FIRST) + (COUNT))                                                      \
+    acc[m][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((F).b[m][j], (F).a[i], acc[m][j][i], 0, 0, 0); \
+  }
+  constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
+  constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
+
+  // Prologue: fill every buffer of the ring, then wait for stage 0.
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s, s * BK);
+  wait_stages<LOADS, STAGES - 1>(nk - 1 < STAGES - 1 ? nk - 1 : STAGES - 1);
+  __syncthreads();
+  Frags cur = read_frags(0, 0);
+  // K steps of one stage but the last: the next step's fragments are read
+  // while this step's MFMAs issue.
+#define MOE_INNER_STEPS(BUF)                                       \
+  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {     \
+  const Frags nxt = read_frags((BUF), ks + 1);                   \
+  MOE_MFMAS(cur, 0, NMFMA)                                       \
+  _Pragma("unroll") for (int g = 0; g < NREAD; ++g) {            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           \
+  }                                                              \
+  __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0); \
+  __builtin_amdgcn_sched_barrier(0);                             \
+  cur = nxt;                                                     \
+  }
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int buf = kt % STAGES;
+    MOE_INNER_STEPS(buf)
+    // Last K step of the stage: half of its MFMAs keep the matrix cores busy
+    // across the stage boundary.
+    MOE_MFMAS(cur, 0, NMFMA / 2)
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage kt+1 has landed once only the stages issued after it are in flight.
+    const int newer = (nk - 2 - kt) < (STAGES - 2) ? (nk - 2 - kt) : (STAGES - 2);
+    wait_stages<LOADS, STAGES - 2>(newer);
+    wait_lgkm0();     // this wave's reads of stage kt are complete
+    __syncthreads();  // stage kt+1 visible to all; buffer kt is free for stage kt+STAGES
+    __builtin_amdgcn_sched_barrier(0);
+    const Frags nxt = read_frags((kt + 1) % STAGES, 0);
+    if (kt + STAGES < nk) issue(buf, (kt + STAGES) * BK);
+    MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+  {  // the last stage
+    const int buf = (nk - 1) % STAGES;
+    MOE_INNER_STEPS(buf)
+    MOE_MFMAS(cur, 0, NMFMA)
+  }
+#undef MOE_INNER_STEPS
+#undef MOE_MFMAS
+
+  // Epilogue: lane holds, for token row m = lane % 32 of each 32-row block,
+  // output columns q*8 + (lane/32)*4 + 0..3 (q = 0..3) of each 32-column block.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = wm * WT_M + i * 32 + (lane & 31);
+    if (m >= valid) continue;
+    const int64_t row = (int64_t)row0 + m;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
+        float g[4], u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          g[r] = acc[0][j][i][q * 4 + r];
+          u[r] = acc[NMAT - 1][j][i][q * 4 + r];
+        }
+        store4<EPI>(C, row, N, n, g, u);
+      }
+  }
+  wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
+  __syncthreads();  // the next item's first stages overwrite LDS
+}
+
+template <int BM, int BN, bool DUAL>
+constexpr int big_lds_bytes(int stages) {
+  return stages * (BM + (DUAL ? 2 : 1) * BN) * 128;
+}
+
+// Persistent kernel over (row tile, column block) items.  With G workgroups
+// and W items, the first floor(W / G) * G items run at full width (every
+// workgroup gets the same number); each remaining item is split into two
+// half-width pieces, so the last round costs about half a full item instead of
+// leaving most CUs idle behind a few full ones.
 template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES>
 __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const uint16_t* __restrict__ A,    // [R_cap, K] bf16 (x_perm or act)
@@ -172,169 +338,39 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
     int64_t R_cap, int E_loc, void* __restrict__ C) {
-  constexpr int NWAVES = 4, WN = 2;
-  constexpr int NMAT = DUAL ? 2 : 1;
-  constexpr int BROWS = NMAT * BN;               // weight rows staged per stage
-  constexpr int A_BYTES = BM * 128, B_BYTES = BROWS * 128;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int WT_M = BM / 2, WT_N = BN / WN;
-  constexpr int TM = WT_M / 32, TN = WT_N / 32;
-  constexpr int LOADS = (BM + BROWS) / 8 / NWAVES;  // direct-to-LDS loads per wave per stage
-  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  static_assert(STAGES >= 2 && STAGES <= 3 && (STAGES - 1) * LOADS < 64, "vmcnt range");
-
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN, DUAL>(STAGES)];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = gridDim.x;
   const int vid = xcd_remap(blockIdx.x, G);
   int nt = *num_tiles;
   if (nt > tiles_cap) nt = (int)tiles_cap;
   const int nbn = N / BN;
   const int64_t total = (int64_t)nt * nbn;
-  const int nk = K / BK;
-  const int64_t b_expert = (int64_t)N * K;
-  for (int64_t item = vid; item < total; item += G) {
+  const int64_t full = total / G * G;  // items run at full width
+
+  // Item -> (expert, first row, real rows, first column); false if the tile entry is inconsistent.
+  auto coords = [&](int64_t item, int& le, int& row0, int& valid, int& n0) {
     int tile_i, nb;
     item_coords<ORDER>(item, nt, nbn, tile_i, nb);
-    const int le = tiles[2 * tile_i];
-    const int row0 = tiles[2 * tile_i + 1];
-    if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) continue;  // block-uniform
-    int valid = counts[le] - (row0 - offsets[le]);
+    le = tiles[2 * tile_i];
+    row0 = tiles[2 * tile_i + 1];
+    if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) return false;
+    valid = counts[le] - (row0 - offsets[le]);
     valid = valid < BM ? valid : BM;
-    const int n0 = nb * BN;
-    // Buffer resources based at this item's operand panels (ranges of a few MiB,
-    // out-of-range reads return zeros).  A and B share the row stride K, so one
-    // per-lane byte offset serves every direct-to-LDS load of this wave:
-    // row (q * NWAVES + wave) * 8 + lane / 8, logical chunk swizzled for that row.
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
-    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
-    const __amdgpu_buffer_rsrc_t rb1 = DUAL ? make_rsrc(B1 + le * b_expert + (int64_t)n0 * K, BN * K * 2) : rb0;
-    const int r_in = lane >> 3;
-    const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
-    floatx16 acc[NMAT][TN][TM];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[m][j][i][v] = 0.f;
-    auto issue = [&](int stage, int k0) {
-      char* s = smem + stage * STAGE;
-#pragma unroll
-      for (int q = 0; q < BM / (8 * NWAVES); ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(s + (q * NWAVES + wave) * 1024), 16, voff,
-                                                 (q * 8 * NWAVES * K + k0) * 2, 0, 0);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int q = 0; q < BN / (8 * NWAVES); ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? rb1 : rb0,
-                                                   (lds_void*)(s + A_BYTES + m * BN * 128 + (q * NWAVES + wave) * 1024),
-                                                   16, voff, (q * 8 * NWAVES * K + k0) * 2, 0, 0);
-    };
-    struct Frags {
-      bf16x8 a[TM];
-      bf16x8 b[NMAT][TN];
-    };
-    auto read_frags = [&](int stage, int ks) {
-      const char* sA = smem + stage * STAGE;
-      const char* sB = sA + A_BYTES;
-      const int chunk = ks * 2 + (lane >> 5);
-      Frags f;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) f.a[i] = lds_frag(sA, wm * WT_M + i * 32 + (lane & 31), chunk);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) f.b[m][j] = lds_frag(sB, m * BN + wn * WT_N + j * 32 + (lane & 31), chunk);
-      return f;
-    };
-// MFMAs number [first, first + count) of one 16-wide K step (order: matrix, column block, row block).
-#define MOE_MFMAS(F, FIRST, COUNT)                                                                        \
-  _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                                        \
-  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                          \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                                        \
-    const int idx_ = (m * TN + j) * TM + i;                                                               \
-    if (idx_ >= (FIRST) && idx_ < (FIRST) + (COUNT))                                                      \
-      acc[m][j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((F).b[m][j], (F).a[i], acc[m][j][i], 0, 0, 0); \
-  }
-    constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
-    constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
+    n0 = nb * BN;
+    return true;
+  };
 
-    // Prologue: fill every buffer of the ring, then wait for stage 0.
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < nk) issue(s, s * BK);
-    wait_stages<LOADS, STAGES - 1>(nk - 1 < STAGES - 1 ? nk - 1 : STAGES - 1);
-    __syncthreads();
-    Frags cur = read_frags(0, 0);
-    // K steps of one stage but the last: the next step's fragments are read
-    // while this step's MFMAs issue.
-#define MOE_INNER_STEPS(BUF)                                       \
-  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {     \
-    const Frags nxt = read_frags((BUF), ks + 1);                   \
-    MOE_MFMAS(cur, 0, NMFMA)                                       \
-    _Pragma("unroll") for (int g = 0; g < NREAD; ++g) {            \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           \
-    }                                                              \
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0); \
-    __builtin_amdgcn_sched_barrier(0);                             \
-    cur = nxt;                                                     \
+  for (int64_t item = vid; item < full; item += G) {
+    int le, row0, valid, n0;
+    if (!coords(item, le, row0, valid, n0)) continue;  // block-uniform
+    gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, wave, lane);
   }
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      const int buf = kt % STAGES;
-      MOE_INNER_STEPS(buf)
-      // Last K step of the stage: half of its MFMAs keep the matrix cores busy
-      // across the stage boundary.
-      MOE_MFMAS(cur, 0, NMFMA / 2)
-      __builtin_amdgcn_sched_barrier(0);
-      // Stage kt+1 has landed once only the stages issued after it are in flight.
-      const int newer = (nk - 2 - kt) < (STAGES - 2) ? (nk - 2 - kt) : (STAGES - 2);
-      wait_stages<LOADS, STAGES - 2>(newer);
-      wait_lgkm0();     // this wave's reads of stage kt are complete
-      __syncthreads();  // stage kt+1 visible to all; buffer kt is free for stage kt+STAGES
-      __builtin_amdgcn_sched_barrier(0);
-      const Frags nxt = read_frags((kt + 1) % STAGES, 0);
-      if (kt + STAGES < nk) issue(buf, (kt + STAGES) * BK);
-      MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
-      __builtin_amdgcn_sched_barrier(0);
-      cur = nxt;
-    }
-    {  // the last stage
-      const int buf = (nk - 1) % STAGES;
-      MOE_INNER_STEPS(buf)
-      MOE_MFMAS(cur, 0, NMFMA)
-    }
-#undef MOE_INNER_STEPS
-#undef MOE_MFMAS
-
-    // Epilogue: lane holds, for token row m = lane % 32 of each 32-row block,
-    // output columns q*8 + (lane/32)*4 + 0..3 (q = 0..3) of each 32-column block.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = wm * WT_M + i * 32 + (lane & 31);
-      if (m >= valid) continue;
-      const int64_t row = (int64_t)row0 + m;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
-          float g[4], u[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            g[r] = acc[0][j][i][q * 4 + r];
-            u[r] = acc[NMAT - 1][j][i][q * 4 + r];
-          }
-          store4<EPI>(C, row, N, n, g, u);
-        }
-    }
-    wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
-    __syncthreads();  // the next item's first stages overwrite LDS
+  for (int64_t piece = vid; piece < 2 * (total - full); piece += G) {
+    int le, row0, valid, n0;
+    if (!coords(full + piece / 2, le, row0, valid, n0)) continue;
+    gemm_item<BM, BN / 2, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0 + (int)(piece % 2) * (BN / 2),
+                                             0, K, C, wave, lane);
   }
 }
 
@@ -485,8 +521,8 @@ int64_t persistent_grid(int64_t max_items) {
 
 template <typename Kern>
 hipError_t launch_persistent(Kern kern, int threads, int64_t max_items, const uint16_t* A, const uint16_t* B0,
-                             const uint16_t* B1, int N, int K, const FfnArgs& a, void* C, hipStream_t s) {
-  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items)), dim3(threads), 0, s, A, B0, B1, N, K,
+                             const uint16_t* B1, int N, int K, const FfnArgs& a, void* C) {
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items)), dim3(threads), 0, a.stream, A, B0, B1, N, K,
                      a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, C);
   return hipGetLastError();
 }
@@ -494,46 +530,46 @@ hipError_t launch_persistent(Kern kern, int threads, int64_t max_items, const ui
 // tile_m >= 128: layer0 = BM x (BN0 gate + BN0 up) (GELU: BM x BN0), layer1 = BM x BN1
 // (BM x 128 when H is not a multiple of BN1).
 template <int BM, int BN0, int ST0, int BN1, int ST1>
-hipError_t launch_big(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_big(const FfnArgs& a) {
   hipError_t e;
   if (a.act == MOE_ACT_SWIGLU_I)
     e = launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, s);
+                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf);
   else
     e = launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, s);
+                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf);
   if (e != hipSuccess) return e;
   if (a.H % BN1 == 0)
-    return launch_persistent(gemm_mfma32_kernel<BM, BN1, false, EPI_F32, ORDER_N, ST1>, 256,
-                             a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+    return launch_persistent(gemm_mfma32_kernel<BM, BN1, false, EPI_F32, ORDER_N, ST1>, 256, a.tiles_cap * (a.H / BN1),
+                             a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
   return launch_persistent(gemm_mfma32_kernel<BM, 128, false, EPI_F32, ORDER_N, ST0>, 256, a.tiles_cap * (a.H / 128),
-                           a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+                           a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
 }
 
 // tile_m <= 64: weight-streaming shapes.
 template <int BM, int WM, int WN, int BN0, int BN1, int WM1, int WN1>
-hipError_t launch_small(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_small(const FfnArgs& a) {
   hipError_t e;
   if (a.act == MOE_ACT_SWIGLU_I)
     e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, true, EPI_SWIGLU, ORDER_M>, WM * WN * 64,
-                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, s);
+                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf);
   else
     e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, false, EPI_GELU, ORDER_M>, WM * WN * 64,
-                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, s);
+                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf);
   if (e != hipSuccess) return e;
   return launch_persistent(gemm_mfma16_kernel<BM, BN1, WM1, WN1, false, EPI_F32, ORDER_N>, WM1 * WN1 * 64,
-                           a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, s);
+                           a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
 }
 
 }  // namespace
 
-hipError_t launch_grouped_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_grouped_ffn(const FfnArgs& a) {
   switch (a.tile_m) {
-    case 256: return launch_big<256, 128, 2, 256, 2>(a, s);
-    case 128: return launch_big<128, 128, 3, 256, 3>(a, s);
-    case 64: return launch_small<64, 1, 8, 128, 128, 1, 8>(a, s);
-    case 32: return launch_small<32, 1, 8, 128, 128, 1, 8>(a, s);
-    case 16: return launch_small<16, 1, 8, 128, 128, 1, 8>(a, s);
+    case 256: return launch_big<256, 128, 2, 256, 2>(a);
+    case 128: return launch_big<128, 128, 3, 256, 3>(a);
+    case 64: return launch_small<64, 1, 8, 128, 128, 1, 8>(a);
+    case 32: return launch_small<32, 1, 8, 128, 128, 1, 8>(a);
+    case 16: return launch_small<16, 1, 8, 128, 128, 1, 8>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -131,7 +131,8 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, con
   a.tiles_cap = tiles_cap;
   a.act_buf = static_cast<uint16_t*>(act_buf);
   a.y_perm = y_perm;
-  return launched(moe::launch_grouped_ffn(a, static_cast<hipStream_t>(stream)));
+  a.stream = static_cast<hipStream_t>(stream);
+  return launched(moe::launch_grouped_ffn(a));
 }
 
 moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int32_t k,
