@@ -7,33 +7,39 @@
 // reorganisation exposes only the data each tile needs.
 //
 // The (token, slot) pairs of local experts are stably counting-sorted on the
-// bucket key b = local_expert * num_ranks + src_rank, visiting pairs in token
-// order, which yields the order (expert, rank, token).  Three launches, no
-// atomics deciding any order (the result is bit-identical run to run):
-//   A  hist:    one wavefront per 64-token chunk c; for every bucket b a
-//               ballot gives each pair its rank inside (b, c) and the count
-//               hist[b][c].
-//   B  scan:    one block: exclusive scan of hist in (b, c) order, per-expert
-//               counts, tile-padded offsets, the base row of every (b, c),
+// bucket key b = local_expert * num_ranks + src_rank, visiting tokens in order,
+// which yields the order (expert, rank, token).  Three launches, no atomics
+// deciding any order (the result is bit-identical run to run):
+//   A  count:   one block per chunk of 256 tokens.  Each wavefront ranks its
+//               pairs inside their bucket with a ballot multisplit over the
+//               bits of the bucket id (the rank of a pair is the number of
+//               lower lanes holding the same bucket in any slot; a token has
+//               at most one pair per bucket); per-wavefront counts in LDS turn
+//               those into ranks inside the chunk and the chunk's count per
+//               bucket, hist[b][c].
+//   B  scan:    one block: exclusive scan of hist in (bucket, chunk) order
+//               with 16-byte loads, per-expert counts, tile-padded offsets,
 //               padding markers in row_src, and the tile list ordered by
 //               (priority, expert, m-tile) with a stable partition on priority.
 //   D  scatter: one wavefront per token: row of each local pair =
-//               base[b][c] + rank, written to row_src / inv_perm, and the
-//               token's row copied once from HBM to each of its rows in
-//               16-byte chunks.
+//               offsets[expert] + (prefix of its bucket and chunk - prefix of
+//               the expert) + rank in chunk, written to row_src / inv_perm, and
+//               the token's row copied once from HBM to each of its rows with
+//               the whole row in flight (16-byte loads).
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kChunk = 64;          // tokens per chunk (one wavefront)
+constexpr int kChunk = 256;         // tokens per chunk (one block of kernel A)
 constexpr int kScanThreads = 1024;  // block size of kernel B
 constexpr int kMaxExperts = 4096;   // E_loc * num_ranks <= 4096 (validated on the host)
+constexpr int kMaxBits = 12;        // bits of a bucket id (4096 buckets)
 
 struct WsLayout {
   int64_t nb, nc;
-  int32_t* hist;   // [nb * nc]
-  int32_t* lrank;  // [T * k]
+  int32_t* hist;   // [nb * nc], then exclusive prefix
+  int32_t* lrank;  // [T * k], rank of the pair inside its bucket and chunk, -1 if not local
 };
 
 __host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -56,41 +62,84 @@ __device__ __forceinline__ int clamp_rank(const int32_t* src_rank, int64_t t, in
 }
 
 // ---------------------------------------------------------------------------
-// A: per-chunk bucket counts and in-chunk stable ranks
+// A: ranks inside (bucket, chunk) and per-chunk bucket counts
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ topk_idx,
-                                                           const int32_t* __restrict__ src_rank,
-                                                           int64_t T, int k, int expert_begin,
-                                                           int E_loc, int R, int32_t* __restrict__ hist,
-                                                           int32_t* __restrict__ lrank, int64_t nb,
-                                                           int64_t nc) {
-  const int lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
-  if (c >= nc) return;
-  const int64_t t = c * kChunk + lane;
+// Dynamic LDS: bucket[k][256] ints, then count[4 wavefronts][nb] ints.
+__global__ __launch_bounds__(kChunk) void permute_count_kernel(const int32_t* __restrict__ topk_idx,
+                                                               const int32_t* __restrict__ src_rank, int64_t T,
+                                                               int k, int expert_begin, int E_loc, int R, int nbits,
+                                                               int32_t* __restrict__ hist,
+                                                               int32_t* __restrict__ lrank, int64_t nb, int64_t nc) {
+  extern __shared__ int32_t sh[];
+  int32_t* s_bucket = sh;                 // [k][kChunk]
+  int32_t* s_count = sh + k * kChunk;     // [4][nb]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t c = blockIdx.x;
+  const int64_t t = c * kChunk + tid;
   const bool valid = t < T;
   const int r = valid ? clamp_rank(src_rank, t, R) : 0;
 
-  int bucket[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    bucket[j] = -1;
-    if (j < k && valid) {
+  for (int j = 0; j < k; ++j) {
+    int b = -1;
+    if (valid) {
       const int le = topk_idx[t * k + j] - expert_begin;
-      if (le >= 0 && le < E_loc) bucket[j] = le * R + r;
-      else lrank[t * k + j] = -1;
+      if (le >= 0 && le < E_loc) b = le * R + r;
+    }
+    s_bucket[j * kChunk + tid] = b;
+  }
+  for (int64_t i = tid; i < 4 * nb; i += kChunk) s_count[i] = 0;
+  __syncthreads();
+
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Rank of each of this lane's pairs among the wavefront's pairs with the same
+  // bucket, and that bucket's count in the wavefront.  The other lanes' slot jp
+  // is compared with all of this lane's slots at once: a lane matches when its
+  // bucket agrees on every bit, tested against one ballot per bit.  Rank (< 64)
+  // and count (<= 64) are packed into one int as rank | count << 16.
+  int packed[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) packed[j] = 0;
+  for (int jp = 0; jp < k; ++jp) {
+    const int bo = s_bucket[jp * kChunk + tid];
+    const uint64_t vm = __ballot(bo >= 0);
+    uint64_t bits[kMaxBits];
+#pragma unroll
+    for (int bit = 0; bit < kMaxBits; ++bit) bits[bit] = bit < nbits ? __ballot(bo >= 0 && ((bo >> bit) & 1)) : 0ull;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j < k) {
+        const int b = s_bucket[j * kChunk + tid];
+        uint64_t m = vm;
+#pragma unroll
+        for (int bit = 0; bit < kMaxBits; ++bit)
+          if (bit < nbits) m &= ((b >> bit) & 1) ? bits[bit] : ~bits[bit];
+        packed[j] += (int)__popcll(m & below) | ((int)__popcll(m) << 16);
+      }
     }
   }
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t b = 0; b < nb; ++b) {
-    int jj = -1;
+  // Each bucket present in this wavefront has exactly one pair with rank 0: it publishes the count.
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < k && bucket[j] == (int)b) jj = j;
-    const uint64_t m = __ballot(jj >= 0);
-    if (jj >= 0) lrank[t * k + jj] = __popcll(m & lt);
-    if (lane == 0) hist[b * nc + c] = __popcll(m);
+  for (int j = 0; j < 32; ++j) {
+    if (j < k) {
+      const int b = s_bucket[j * kChunk + tid];
+      if (b >= 0 && (packed[j] & 0xFFFF) == 0) s_count[(int64_t)w * nb + b] = packed[j] >> 16;
+    }
   }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    if (j < k && valid) {
+      const int b = s_bucket[j * kChunk + tid];
+      int rk = -1;
+      if (b >= 0) {
+        rk = packed[j] & 0xFFFF;
+        for (int wp = 0; wp < w; ++wp) rk += s_count[(int64_t)wp * nb + b];
+      }
+      lrank[t * k + j] = rk;
+    }
+  }
+  for (int64_t b = tid; b < nb; b += kChunk)
+    hist[b * nc + c] = s_count[b] + s_count[nb + b] + s_count[2 * nb + b] + s_count[3 * nb + b];
 }
 
 // ---------------------------------------------------------------------------
@@ -140,18 +189,46 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
   const int tid = threadIdx.x;
   const int64_t N = nb * nc;
 
-  // 1. exclusive scan of hist in (bucket, chunk) order
-  const int64_t seg = (N + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = (int64_t)tid * seg, hi = lo + seg < N ? lo + seg : N;
-  int s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += hist[i];
-  int total;
-  int run = block_excl_scan(s, sh, &total);
-  for (int64_t i = lo; i < hi; ++i) {
-    const int h = hist[i];
-    hist[i] = run;
-    run += h;
+  // 1. exclusive scan of hist in (bucket, chunk) order, 16 consecutive entries
+  //    per thread per pass (four 16-byte loads in flight when aligned and in range)
+  constexpr int V = 16;
+  int carry = 0;
+  for (int64_t base = 0; base < N; base += (int64_t)kScanThreads * V) {
+    const int64_t lo = base + (int64_t)tid * V;
+    int v[V];
+    if (lo + V <= N) {
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        const intx4 x = *reinterpret_cast<const intx4*>(hist + lo + 4 * q);
+        v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < V; ++q) v[q] = lo + q < N ? hist[lo + q] : 0;
+    }
+    int s = 0;
+#pragma unroll
+    for (int q = 0; q < V; ++q) s += v[q];
+    int tot;
+    int run = carry + block_excl_scan(s, sh, &tot);
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const int h = v[q];
+      v[q] = run;
+      run += h;
+    }
+    if (lo + V <= N) {
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q)
+        *reinterpret_cast<intx4*>(hist + lo + 4 * q) = intx4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < V; ++q)
+        if (lo + q < N) hist[lo + q] = v[q];
+    }
+    carry += tot;
   }
+  const int total = carry;
   __syncthreads();
 
   // 2. per-expert unpadded starts, counts, padded offsets, tile starts
@@ -190,22 +267,15 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
   }
   __syncthreads();
 
-  // 3. base row of every (bucket, chunk): padded start + rank inside expert
-  for (int64_t i = tid; i < N; i += kScanThreads) {
-    const int le = (int)(i / nc / R);
-    hist[i] = s_off[le] + hist[i] - s_us[le];
-  }
-
-  // 4. padding rows and the unused tail carry -1 in row_src
+  // 3. padding rows and the unused tail carry -1 in row_src
   for (int64_t i = tid; i < (int64_t)E_loc * tile_m; i += kScanThreads) {
     const int le = (int)(i / tile_m), q = (int)(i % tile_m);
     const int64_t row = (int64_t)s_off[le] + (s_us[le + 1] - s_us[le]) + q;
     if (row < s_off[le + 1]) row_src[row] = -1;
   }
   for (int64_t row = (int64_t)s_off[E_loc] + tid; row < R_cap; row += kScanThreads) row_src[row] = -1;
-  __syncthreads();  // hist now holds base rows; step 5 reads them
 
-  // 5. tile list, stably partitioned on priority (= rank of the tile's last row)
+  // 4. tile list, stably partitioned on priority (= rank of the tile's last row)
   const int nt = s_tb[E_loc] < tiles_cap ? s_tb[E_loc] : (int)tiles_cap;
   if (tid == 0) *num_tiles = nt;
   int placed = 0;
@@ -225,7 +295,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
         const int last = ((m + 1) * tile_m < cnt ? (m + 1) * tile_m : cnt) - 1;
         prio = 0;
         for (int r = 1; r < R; ++r) {
-          const int cum = hist[((int64_t)le * R + r) * nc] - s_off[le];
+          const int cum = hist[((int64_t)le * R + r) * nc] - s_us[le];  // rows of expert le with rank < r
           if (cum <= last) prio = r;
         }
       }
@@ -247,19 +317,20 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const intx4* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ src_rank, int64_t T, int H, int k, int expert_begin, int E_loc, int R,
-    int64_t R_cap, const int32_t* __restrict__ base, const int32_t* __restrict__ lrank, int64_t nc,
-    intx4* __restrict__ x_perm, int32_t* __restrict__ row_src, int32_t* __restrict__ inv_perm) {
+    int64_t R_cap, const int32_t* __restrict__ prefix, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ lrank, int64_t nc, intx4* __restrict__ x_perm, int32_t* __restrict__ row_src,
+    int32_t* __restrict__ inv_perm) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= T) return;  // whole wave exits together
   int p = -1;
   if (lane < k) {
     const int le = topk_idx[t * k + lane] - expert_begin;
     if (le >= 0 && le < E_loc) {
       const int r = clamp_rank(src_rank, t, R);
       const int64_t b = (int64_t)le * R + r;
-      p = base[b * nc + t / kChunk] + lrank[t * k + lane];
-      if (p >= R_cap) p = -1;  // inconsistent input; never write out of bounds
+      p = offsets[le] + (prefix[b * nc + t / kChunk] - prefix[(int64_t)le * R * nc]) + lrank[t * k + lane];
+      if (p < 0 || p >= R_cap) p = -1;  // inconsistent input; never write out of bounds
       if (p >= 0) row_src[p] = (int32_t)(t * k + lane);
     }
     inv_perm[t * k + lane] = p;
@@ -275,7 +346,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   if (!any) return;
   const int nch = H / 8;  // 16-byte chunks per row
   const intx4* src = x + t * nch;
-  constexpr int U = 4;
+  constexpr int U = 8;    // up to 8 x 16 B per lane in flight: an 8 KiB row per pass
   for (int c0 = lane; c0 < nch; c0 += kWave * U) {
     intx4 v[U];
 #pragma unroll
@@ -301,16 +372,23 @@ size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks) {
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   WsLayout L = ws_layout(a.ws, a.T, a.k, a.E_loc, a.num_ranks);
-  const int wpb = 4;  // wavefronts per block
-  hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)((L.nc + wpb - 1) / wpb)), dim3(wpb * kWave), 0, s,
-                     a.topk_idx, a.src_rank, a.T, a.k, a.expert_begin, a.E_loc, a.num_ranks, L.hist,
-                     L.lrank, L.nb, L.nc);
+  int nbits = 0;
+  while ((1ll << nbits) < L.nb) ++nbits;
+  const size_t count_lds = ((size_t)a.k * kChunk + 4 * (size_t)L.nb) * sizeof(int32_t);  // <= 96 KiB
+  if (count_lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_count_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)count_lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)L.nc), dim3(kChunk), count_lds, s, a.topk_idx, a.src_rank,
+                     a.T, a.k, a.expert_begin, a.E_loc, a.num_ranks, nbits, L.hist, L.lrank, L.nb, L.nc);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, L.hist, L.nb, L.nc, a.E_loc,
                      a.num_ranks, a.tile_m, a.R_cap, a.tiles_cap, a.counts, a.offsets, a.row_src, a.tiles,
                      a.num_tiles);
+  const int wpb = 4;  // wavefronts per block
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((a.T + wpb - 1) / wpb)), dim3(wpb * kWave), 0, s,
-                     reinterpret_cast<const intx4*>(a.x), a.topk_idx, a.src_rank, a.T, a.H, a.k,
-                     a.expert_begin, a.E_loc, a.num_ranks, a.R_cap, L.hist, L.lrank, L.nc,
+                     reinterpret_cast<const intx4*>(a.x), a.topk_idx, a.src_rank, a.T, a.H, a.k, a.expert_begin,
+                     a.E_loc, a.num_ranks, a.R_cap, L.hist, a.offsets, L.lrank, L.nc,
                      reinterpret_cast<intx4*>(a.x_perm), a.row_src, a.inv_perm);
   return hipGetLastError();
 }
