@@ -51,7 +51,56 @@ def parse():
     ap.add_argument("--workload", default="mixtral", choices=list(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle sample budget in seconds (0 disables the CPU baseline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the HBM byte "
+                         "counters FETCH_SIZE / WRITE_SIZE against a known size) and exit")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant call, measured with rocprofv3 counters on the same
+# kernel sources (profiles/hbm_traffic_grouped_ffn.md); reported only while the
+# kernel sources still hash to the values recorded there.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_grouped_ffn.md")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_moe_amd", "csrc", f)
+                for f in ("grouped_gemm.hip", "common.h")]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """Scaled HBM bytes per moe_grouped_ffn launch from the counter summary, or None if stale/absent."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256") != gemm_source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "copies": 5}), flush=True)
 
 
 def cpu_baseline(cfg, d, seconds):
@@ -114,6 +163,10 @@ def main():
         print("bench.py measures one GPU's share of the layer; runs on more than one GPU are not "
               "part of this build (use --gpus 1).", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from mixture_experts_layer_moe_amd import workloads as W
@@ -186,7 +239,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload),
         },
         "cpu_baseline": None,
     }
