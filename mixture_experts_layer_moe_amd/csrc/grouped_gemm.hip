@@ -167,8 +167,14 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 
 // One work item: rows [row0, row0 + BM) of expert le (valid of them real) times
 // output columns [n0, n0 + BN), reduction over [k_begin, k_begin + k_len).
+//
+// smem is deliberately not restrict-qualified: a restrict LDS pointer gives
+// the LDS accesses alias-scope metadata after inlining, and with it the
+// compiler starts matching LDS reads against the direct-to-LDS loads still in
+// flight and inserts full vmcnt(0) drains inside the K loop.  The ring is
+// synchronised by the explicit waits below instead.
 template <int BM, int BN, bool DUAL, int EPI, int STAGES>
-__device__ __forceinline__ void gemm_item(char* __restrict__ smem, const uint16_t* __restrict__ A,
+__device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
                                           int N, int K, int le, int row0, int valid, int n0, int k_begin, int k_len,
                                           void* __restrict__ C, int wave, int lane) {
