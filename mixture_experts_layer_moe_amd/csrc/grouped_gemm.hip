@@ -34,10 +34,17 @@
 //     (row & 7) ^ ((row >> 3) & 1), so that the fragment reads (consecutive
 //     lanes read consecutive rows at one chunk) hit distinct banks both for
 //     8 lanes within 128 B and for 16 lanes within 256 B.
+//   * Big tiles: the loads of stage kt + STAGES - 1 are spread over the first
+//     K steps of stage kt, one after an MFMA, into the ring buffer freed at
+//     the previous barrier (a burst of them right after the barrier backs up
+//     the CU's address unit and stalls the issuing waves' matrix cores).
+//     Stages past the end load through a buffer resource with no records,
+//     so every iteration runs the same schedule.
 //   * The stage boundary is software-pipelined: the wait for the next stage,
 //     the barrier and the next stage's first fragment reads are issued
 //     before the last MFMAs of the current stage, which keep the matrix
-//     cores busy meanwhile.
+//     cores busy meanwhile.  The barrier is a bare s_barrier after explicit
+//     waits, so the stages in flight stay in flight across it.
 //   * Big tiles (tile_m >= 128): 4 waves (one per SIMD), each owning a
 //     128 x 128 (or 64 x 128) accumulator tile of v_mfma_f32_32x32x16_bf16,
 //     which keeps LDS traffic per flop at half of the LDS bandwidth.  Small
@@ -114,12 +121,33 @@ __device__ __forceinline__ bf16x8 lds_frag(const char* tile, int row, int chunk)
 // s_waitcnt lgkmcnt(0), other counters left alone.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
+// Workgroup barrier of an LDS ring.  The caller has already waited for its own
+// LDS reads (lgkmcnt) and for the direct-to-LDS loads that must have landed
+// (vmcnt); the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.  __syncthreads() would in addition make the
+// compiler wait for every direct-to-LDS load still in flight, draining the
+// stages the ring keeps in flight across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until at most n * per direct-to-LDS loads of this wave are in flight (n small, runtime).
 template <int per, int max_n>
 __device__ __forceinline__ void wait_stages(int n) {
   if (max_n >= 2 && n >= 2) wait_vmcnt<(max_n >= 2 ? 2 * per : 0)>();
   else if (max_n >= 1 && n >= 1) wait_vmcnt<(max_n >= 1 ? per : 0)>();
   else wait_vmcnt<0>();
+}
+
+// Memory operation t of one K step that issues nread fragment reads and nload
+// direct-to-LDS loads: the reads first (the next step needs them), then the
+// loads; the index of the read (>= 0) or -1 - the index of the load.  The LDS
+// reads and the loads stay in program order (the compiler cannot tell they
+// touch different buffers), so this is the order they issue in.
+__host__ __device__ constexpr int step_slot(int t, int nread, int nload) {
+  return t < nread ? t : -1 - (t - nread);
 }
 
 // Work item -> (tile index, column block).
@@ -188,6 +216,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int LOADS = (BM + BROWS) / 8 / NWAVES;  // direct-to-LDS loads per wave per stage
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(STAGES >= 2 && STAGES <= 3 && (STAGES - 1) * LOADS < 64, "vmcnt range");
+  constexpr int A_PIECES = BM / (8 * NWAVES), B_PIECES = BN / (8 * NWAVES);  // loads per wave: A, each weight matrix
   const int wm = wave / WN, wn = wave % WN;
   const int nk = k_len / BK;
   const int64_t b_expert = (int64_t)N * K;
@@ -199,6 +228,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
   const __amdgpu_buffer_rsrc_t rb1 = DUAL ? make_rsrc(B1 + le * b_expert + (int64_t)n0 * K, BN * K * 2) : rb0;
+  const __amdgpu_buffer_rsrc_t rnone = make_rsrc(A, 0);  // no records: every load reads zero, fetches nothing
   const int r_in = lane >> 3;
   const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
   floatx16 acc[NMAT][TN][TM];
@@ -210,23 +240,32 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][j][i][v] = 0.f;
-  auto issue = [&](int stage, int k0) {
-    char* s = smem + stage * STAGE;
-#pragma unroll
-    for (int q = 0; q < BM / (8 * NWAVES); ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(s + (q * NWAVES + wave) * 1024), 16, voff,
-                                               (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int q = 0; q < BN / (8 * NWAVES); ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? rb1 : rb0,
-                                                 (lds_void*)(s + A_BYTES + m * BN * 128 + (q * NWAVES + wave) * 1024),
-                                                 16, voff, (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
+  // Direct-to-LDS load number p (0 <= p < LOADS, a constant after unrolling)
+  // of stage buffer `stage` for K offset k0, through the resources (a, b0, b1):
+  // the first A_PIECES stage 8 * NWAVES token rows each, the rest the rows of
+  // the weight matrices.
+  auto load = [&](int p, int stage, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0,
+                  __amdgpu_buffer_rsrc_t b1) {
+    const bool is_a = p < A_PIECES;
+    const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
+    const int lds_off = (is_a ? 0 : A_BYTES + m * BN * 128) + (q * NWAVES + wave) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a : (m ? b1 : b0), (lds_void*)(smem + stage * STAGE + lds_off), 16,
+                                             voff, (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
   };
   struct Frags {
     bf16x8 a[TM];
     bf16x8 b[NMAT][TN];
+  };
+  // Fragment read r of K step ks: r < TM the token rows, else weight rows.
+  auto read_one = [&](Frags& f, int stage, int ks, int r) {
+    const char* sA = smem + stage * STAGE;
+    const int chunk = ks * 2 + (lane >> 5);
+    if (r < TM) {
+      f.a[r] = lds_frag(sA, wm * WT_M + r * 32 + (lane & 31), chunk);
+    } else {
+      const int m = (r - TM) / TN, j = (r - TM) % TN;
+      f.b[m][j] = lds_frag(sA + A_BYTES, m * BN + wn * WT_N + j * 32 + (lane & 31), chunk);
+    }
   };
   auto read_frags = [&](int stage, int ks) {
     const char* sA = smem + stage * STAGE;
@@ -253,49 +292,86 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
   constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
 
-  // Prologue: fill every buffer of the ring, then wait for stage 0.
+  // Loads of one stage are spread over the first SPREAD K steps of the
+  // previous stage, one after every other MFMA: issued in one burst they back
+  // up the CU's address unit, which stalls the issuing waves (and with them
+  // their matrix cores) for a large part of the stage.
+  constexpr int SPREAD = (2 * LOADS + NMFMA - 1) / NMFMA < BK / 16 - 1 ? (2 * LOADS + NMFMA - 1) / NMFMA : BK / 16 - 1;
+  constexpr int PER_STEP = (LOADS + SPREAD - 1) / SPREAD;
+
+  // Ring schedule: the prologue loads stages 0 .. STAGES-2; iteration kt
+  // (computing stage kt) loads stage kt + STAGES - 1 into buffer
+  // (kt - 1) mod STAGES, which every wave has finished reading at the barrier
+  // that ended iteration kt - 1 (and which the prologue left empty for
+  // kt = 0).  A stage past the end is "loaded" through resources with no
+  // records: every lane reads zero, nothing is fetched, and the zeros land in
+  // that free buffer, so the schedule is the same in every iteration.
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nk) issue(s, s * BK);
-  wait_stages<LOADS, STAGES - 1>(nk - 1 < STAGES - 1 ? nk - 1 : STAGES - 1);
-  __syncthreads();
+  for (int st = 0; st + 1 < STAGES; ++st)
+    if (st < nk)
+#pragma unroll
+      for (int p = 0; p < LOADS; ++p) load(p, st, st * BK, ra, rb0, rb1);
+  {  // stage 0 has landed once only the prologue's later stages are in flight
+    const int later = (nk < STAGES - 1 ? nk : STAGES - 1) - 1;
+    wait_stages<LOADS, STAGES - 2>(later);
+  }
+  ring_barrier();
   Frags cur = read_frags(0, 0);
   // K steps of one stage but the last: the next step's fragments are read
-  // while this step's MFMAs issue.
-#define MOE_INNER_STEPS(BUF)                                       \
-  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {     \
-  const Frags nxt = read_frags((BUF), ks + 1);                   \
-  MOE_MFMAS(cur, 0, NMFMA)                                       \
-  _Pragma("unroll") for (int g = 0; g < NREAD; ++g) {            \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           \
-  }                                                              \
-  __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0); \
-  __builtin_amdgcn_sched_barrier(0);                             \
-  cur = nxt;                                                     \
+  // while this step's MFMAs issue; with LD, steps below SPREAD also issue
+  // their share of the loads of stage TS into buffer TBUF through (RA, RB0, RB1).
+#define MOE_INNER_STEPS(BUF, LD, TBUF, TS, RA, RB0, RB1)                              \
+  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {                        \
+  const int np_ = (LD) && ks < SPREAD                                               \
+                      ? (LOADS - ks * PER_STEP < PER_STEP ? LOADS - ks * PER_STEP : PER_STEP) \
+                      : 0;                                                          \
+  Frags nxt;                                                                        \
+  _Pragma("unroll") for (int t = 0; t < NREAD + np_; ++t) {                         \
+    const int sl = step_slot(t, NREAD, np_);                                        \
+    if (sl >= 0) read_one(nxt, (BUF), ks + 1, sl);                                  \
+    else load(ks * PER_STEP - 1 - sl, (TBUF), (TS) * BK, (RA), (RB0), (RB1));       \
+  }                                                                                 \
+  MOE_MFMAS(cur, 0, NMFMA)                                                          \
+  /* Keep this step's MFMAs ahead of the loads that follow them (MFMAs have no */   \
+  /* side effects, so without a use here they could drift into later steps). */     \
+  if (np_ > 0)                                                                      \
+  _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                  \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                    \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) asm volatile("" : "+a"(acc[m][j][i])); \
+  _Pragma("unroll") for (int t = 0; t < NMFMA || t < NREAD + np_; ++t) {            \
+    if (t < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               \
+    if (t < NREAD + np_) {                                                          \
+      if (step_slot(t, NREAD, np_) >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+      else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                       \
+    }                                                                               \
+  }                                                                                 \
+  __builtin_amdgcn_sched_barrier(0);                                                \
+  cur = nxt;                                                                        \
   }
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int buf = kt % STAGES;
-    MOE_INNER_STEPS(buf)
+    const int ts = kt + STAGES - 1;
+    const bool real = ts < nk;
+    MOE_INNER_STEPS(buf, true, (kt + STAGES - 1) % STAGES, ts, real ? ra : rnone, real ? rb0 : rnone,
+                    real ? rb1 : rnone)
     // Last K step of the stage: half of its MFMAs keep the matrix cores busy
     // across the stage boundary.
     MOE_MFMAS(cur, 0, NMFMA / 2)
     __builtin_amdgcn_sched_barrier(0);
-    // Stage kt+1 has landed once only the stages issued after it are in flight.
-    const int newer = (nk - 2 - kt) < (STAGES - 2) ? (nk - 2 - kt) : (STAGES - 2);
-    wait_stages<LOADS, STAGES - 2>(newer);
+    // Stage kt+1 has landed once only the STAGES - 2 load groups issued after
+    // it (one per iteration) are in flight.
+    wait_vmcnt<(STAGES - 2) * LOADS>();
     wait_lgkm0();     // this wave's reads of stage kt are complete
-    __syncthreads();  // stage kt+1 visible to all; buffer kt is free for stage kt+STAGES
+    ring_barrier();   // stage kt+1 visible to all; buffer kt is free from the next iteration on
     __builtin_amdgcn_sched_barrier(0);
     const Frags nxt = read_frags((kt + 1) % STAGES, 0);
-    if (kt + STAGES < nk) issue(buf, (kt + STAGES) * BK);
     MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
   }
   {  // the last stage
     const int buf = (nk - 1) % STAGES;
-    MOE_INNER_STEPS(buf)
+    MOE_INNER_STEPS(buf, false, 0, 0, ra, rb0, rb1)
     MOE_MFMAS(cur, 0, NMFMA)
   }
 #undef MOE_INNER_STEPS
@@ -345,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
     int64_t R_cap, int E_loc, void* __restrict__ C) {
   __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN, DUAL>(STAGES)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
   const int vid = xcd_remap(blockIdx.x, G);
   int nt = *num_tiles;
