@@ -74,6 +74,12 @@ int64_t moe_tiles_capacity(int64_t T, int32_t k, int32_t E_loc, int32_t tile_m);
 /* Bytes of device workspace moe_permute needs.  Returns 0 on invalid arguments. */
 size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E_loc, int32_t num_ranks);
 
+/* Bytes of optional device workspace for moe_grouped_ffn with this tile_m and
+ * H on the current device (0 for tile_m <= 64, which never uses it; 0 on
+ * invalid arguments).  The workspace holds fp32 partial tiles: one CU-count's
+ * worth of tile_m x 256 (or x 128) blocks. */
+size_t moe_grouped_ffn_workspace_bytes(int32_t tile_m, int32_t H);
+
 /*
  * moe_route_topk -- top-k routing (section 2.1: each token activates only the
  * experts its router selects; the gate weights weight the top-k reduce).
@@ -146,6 +152,11 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
  * untouched.  x_perm, expert_counts, expert_offsets, tiles and num_tiles are
  * moe_permute's outputs for the same tile_m; R_cap and tiles_cap are the
  * capacities they were allocated with.  Accumulation is fp32.
+ * ws / ws_bytes: optional device scratch (NULL / 0 is allowed) of at least
+ * moe_grouped_ffn_workspace_bytes(tile_m, H); with it, the last scheduling
+ * round of layer1 splits its tiles along K into fp32 partials that a second
+ * kernel sums in a fixed order, so the result stays deterministic.  A
+ * non-NULL ws that is too small returns MOE_ERR_WORKSPACE.
  * Requires H % 128 == 0, F % 128 == 0, tile_m in {16, 32, 64, 128, 256}.
  */
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
@@ -153,7 +164,8 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
                            const int32_t* num_tiles, const void* w0, const void* w0_up,
                            const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act,
                            int32_t tile_m, int64_t R_cap, int64_t tiles_cap,
-                           void* act_buf, float* y_perm, void* stream);
+                           void* act_buf, float* y_perm, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * moe_combine -- gather and top-k reduce (section 2.1: expert outputs are

@@ -49,8 +49,10 @@ struct FfnArgs {
   int64_t R_cap, tiles_cap;
   uint16_t* act_buf;
   float* y_perm;
+  void* ws;  // split-K partials of layer1's last round, or null
   hipStream_t stream;
 };
+size_t grouped_ffn_ws_bytes(int tile_m, int H);
 hipError_t launch_grouped_ffn(const FfnArgs& a);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,

@@ -195,6 +195,8 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 
 // One work item: rows [row0, row0 + BM) of expert le (valid of them real) times
 // output columns [n0, n0 + BN), reduction over [k_begin, k_begin + k_len).
+// Output element (m, n0 + c) goes to C[(c_row0 + m) * ldc + c_n0 + c]; only
+// the valid rows are stored.
 //
 // smem is deliberately not restrict-qualified: a restrict LDS pointer gives
 // the LDS accesses alias-scope metadata after inlining, and with it the
@@ -205,7 +207,8 @@ template <int BM, int BN, bool DUAL, int EPI, int STAGES>
 __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
                                           int N, int K, int le, int row0, int valid, int n0, int k_begin, int k_len,
-                                          void* __restrict__ C, int wave, int lane) {
+                                          void* __restrict__ C, int64_t c_row0, int ldc, int c_n0, int wave,
+                                          int lane) {
   constexpr int NWAVES = 4, WN = 2;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BROWS = NMAT * BN;               // weight rows staged per stage
@@ -383,19 +386,19 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   for (int i = 0; i < TM; ++i) {
     const int m = wm * WT_M + i * 32 + (lane & 31);
     if (m >= valid) continue;
-    const int64_t row = (int64_t)row0 + m;
+    const int64_t row = c_row0 + m;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
+        const int n = c_n0 + wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
         float g[4], u[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           g[r] = acc[0][j][i][q * 4 + r];
           u[r] = acc[NMAT - 1][j][i][q * 4 + r];
         }
-        store4<EPI>(C, row, N, n, g, u);
+        store4<EPI>(C, row, ldc, n, g, u);
       }
   }
   wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
@@ -407,19 +410,36 @@ constexpr int big_lds_bytes(int stages) {
   return stages * (BM + (DUAL ? 2 : 1) * BN) * 128;
 }
 
+// Number of K slices of each last-round item (1 = no split) when the rem
+// items left after the whole rounds are split along K: as many slices as fit
+// in one round of G workgroups, at most 4, dividing the nk stages of K.
+__host__ __device__ inline int tail_ksplit(int64_t rem, int G, int nk) {
+  if (rem <= 0) return 1;
+  int S = (int)(G / rem);
+  S = S > 4 ? 4 : S;
+  while (S > 1 && nk % S != 0) --S;
+  return S < 1 ? 1 : S;
+}
+
 // Persistent kernel over (row tile, column block) items.  With G workgroups
-// and W items, the first floor(W / G) * G items run at full width (every
-// workgroup gets the same number); each remaining item is split into two
-// half-width pieces, so the last round costs about half a full item instead of
+// and W items, the first floor(W / G) * G items run whole (every workgroup
+// gets the same number).  The remaining items run in one more round:
+//  * with SPLITK (layer1 only: its epilogue is linear) and S = tail_ksplit
+//    > 1, each is split into S slices of K whose fp32 partial tiles go to ws
+//    (piece p at ws + p * BM * BN, row-major BM x BN); reduce_slices_kernel
+//    sums them in slice order afterwards, so the result is deterministic;
+//  * otherwise each is split into two half-width pieces.
+// Either way the last round costs a fraction of a full item instead of
 // leaving most CUs idle behind a few full ones.
-template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES>
+template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES, bool SPLITK>
 __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const uint16_t* __restrict__ A,    // [R_cap, K] bf16 (x_perm or act)
     const uint16_t* __restrict__ B0,   // [E_loc, N, K] bf16
     const uint16_t* __restrict__ B1,   // [E_loc, N, K] bf16 (DUAL) or null
     int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
-    int64_t R_cap, int E_loc, void* __restrict__ C) {
+    int64_t R_cap, int E_loc, void* __restrict__ C, float* __restrict__ ws) {
+  static_assert(!SPLITK || EPI == EPI_F32, "K slices need a linear epilogue");
   __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN, DUAL>(STAGES)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
@@ -428,7 +448,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
   if (nt > tiles_cap) nt = (int)tiles_cap;
   const int nbn = N / BN;
   const int64_t total = (int64_t)nt * nbn;
-  const int64_t full = total / G * G;  // items run at full width
+  const int64_t full = total / G * G;  // items run whole
+  const int S = SPLITK ? tail_ksplit(total - full, G, K / BK) : 1;
 
   // Item -> (expert, first row, real rows, first column); false if the tile entry is inconsistent.
   auto coords = [&](int64_t item, int& le, int& row0, int& valid, int& n0) {
@@ -446,13 +467,62 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
   for (int64_t item = vid; item < full; item += G) {
     int le, row0, valid, n0;
     if (!coords(item, le, row0, valid, n0)) continue;  // block-uniform
-    gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, wave, lane);
+    gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, row0, N, n0, wave,
+                                         lane);
+  }
+  if (S > 1) {
+    const int k_len = K / S;
+    for (int64_t piece = vid; piece < S * (total - full); piece += G) {
+      int le, row0, valid, n0;
+      if (!coords(full + piece / S, le, row0, valid, n0)) continue;
+      gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, (int)(piece % S) * k_len,
+                                           k_len, ws + piece * (int64_t)(BM * BN), 0, BN, 0, wave, lane);
+    }
+    return;
   }
   for (int64_t piece = vid; piece < 2 * (total - full); piece += G) {
     int le, row0, valid, n0;
     if (!coords(full + piece / 2, le, row0, valid, n0)) continue;
-    gemm_item<BM, BN / 2, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0 + (int)(piece % 2) * (BN / 2),
-                                             0, K, C, wave, lane);
+    const int nh = n0 + (int)(piece % 2) * (BN / 2);
+    gemm_item<BM, BN / 2, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, nh, 0, K, C, row0, N, nh, wave,
+                                             lane);
+  }
+}
+
+// Sums the K slices that gemm_mfma32_kernel<..., SPLITK> left in ws for its
+// last-round items (same G, tile list and shapes) into C's valid rows, slice
+// by slice in order.  Block b covers rows [(b % (BM / RB)) * RB, + RB) of unit
+// b / (BM / RB); launched with G * BM / RB blocks of 256 threads.
+template <int BM, int BN, int ORDER>
+__global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restrict__ ws, int N, int K, int G,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ tiles,
+                                                            const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
+                                                            int64_t R_cap, int E_loc, float* __restrict__ C) {
+  constexpr int RB = 16;
+  int nt = *num_tiles;
+  if (nt > tiles_cap) nt = (int)tiles_cap;
+  const int nbn = N / BN;
+  const int64_t total = (int64_t)nt * nbn, full = total / G * G;
+  const int S = tail_ksplit(total - full, G, K / BK);
+  const int64_t u = blockIdx.x / (BM / RB);
+  const int rc = blockIdx.x % (BM / RB);
+  if (S <= 1 || u >= total - full) return;  // block-uniform
+  int tile_i, nb;
+  item_coords<ORDER>(full + u, nt, nbn, tile_i, nb);
+  const int le = tiles[2 * tile_i], row0 = tiles[2 * tile_i + 1];
+  if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) return;
+  int valid = counts[le] - (row0 - offsets[le]);
+  valid = valid < BM ? valid : BM;
+  const floatx4* part = reinterpret_cast<const floatx4*>(ws + u * S * (int64_t)(BM * BN));
+  for (int e = threadIdx.x; e < RB * (BN / 4); e += 256) {
+    const int m = rc * RB + e / (BN / 4), c4 = e % (BN / 4);
+    if (m >= valid) continue;
+    const int idx = m * (BN / 4) + c4;
+    floatx4 acc = part[idx];
+    for (int q = 1; q < S; ++q) acc += part[q * (BM * BN / 4) + idx];
+    *reinterpret_cast<floatx4*>(C + (int64_t)(row0 + m) * N + nb * BN + c4 * 4) = acc;
   }
 }
 
@@ -601,11 +671,28 @@ int64_t persistent_grid(int64_t max_items) {
   return grid;
 }
 
-template <typename Kern>
+template <typename Kern, typename... Extra>
 hipError_t launch_persistent(Kern kern, int threads, int64_t max_items, const uint16_t* A, const uint16_t* B0,
-                             const uint16_t* B1, int N, int K, const FfnArgs& a, void* C) {
+                             const uint16_t* B1, int N, int K, const FfnArgs& a, void* C, Extra... extra) {
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items)), dim3(threads), 0, a.stream, A, B0, B1, N, K,
-                     a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, C);
+                     a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, C, extra...);
+  return hipGetLastError();
+}
+
+// Layer1 over BM x BN items; with a workspace the last round is split along K.
+template <int BM, int BN, int ST>
+hipError_t launch_layer1(const FfnArgs& a) {
+  const int64_t max_items = a.tiles_cap * (a.H / BN);
+  if (a.ws == nullptr)
+    return launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, false>, 256, max_items, a.act_buf,
+                             a.w1, nullptr, a.H, a.F, a, a.y_perm, (float*)nullptr);
+  hipError_t e = launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, true>, 256, max_items,
+                                   a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, static_cast<float*>(a.ws));
+  if (e != hipSuccess) return e;
+  const int G = (int)persistent_grid(max_items);
+  hipLaunchKernelGGL((reduce_slices_kernel<BM, BN, ORDER_N>), dim3((unsigned)(G * (BM / 16))), dim3(256), 0, a.stream,
+                     static_cast<const float*>(a.ws), a.H, a.F, G, a.counts, a.offsets, a.tiles, a.num_tiles,
+                     a.tiles_cap, a.R_cap, a.E_loc, a.y_perm);
   return hipGetLastError();
 }
 
@@ -615,17 +702,14 @@ template <int BM, int BN0, int ST0, int BN1, int ST1>
 hipError_t launch_big(const FfnArgs& a) {
   hipError_t e;
   if (a.act == MOE_ACT_SWIGLU_I)
-    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf);
+    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0, false>, 256, a.tiles_cap * (a.F / BN0),
+                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, (float*)nullptr);
   else
-    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf);
+    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0, false>, 256, a.tiles_cap * (a.F / BN0),
+                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, (float*)nullptr);
   if (e != hipSuccess) return e;
-  if (a.H % BN1 == 0)
-    return launch_persistent(gemm_mfma32_kernel<BM, BN1, false, EPI_F32, ORDER_N, ST1>, 256, a.tiles_cap * (a.H / BN1),
-                             a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
-  return launch_persistent(gemm_mfma32_kernel<BM, 128, false, EPI_F32, ORDER_N, ST0>, 256, a.tiles_cap * (a.H / 128),
-                           a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
+  if (a.H % BN1 == 0) return launch_layer1<BM, BN1, ST1>(a);
+  return launch_layer1<BM, 128, ST0>(a);
 }
 
 // tile_m <= 64: weight-streaming shapes.
@@ -644,6 +728,13 @@ hipError_t launch_small(const FfnArgs& a) {
 }
 
 }  // namespace
+
+size_t grouped_ffn_ws_bytes(int tile_m, int H) {
+  // Split-K partial tiles of layer1's last round: at most one round of items.
+  if (tile_m < 128) return 0;
+  const int bn = H % 256 == 0 ? 256 : 128;
+  return (size_t)persistent_grid(INT32_MAX) * tile_m * bn * sizeof(float);
+}
 
 hipError_t launch_grouped_ffn(const FfnArgs& a) {
   switch (a.tile_m) {

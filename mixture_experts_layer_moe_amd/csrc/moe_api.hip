@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool tile_m_ok(int32_t tm) { return tm == 16 || tm == 32 || tm == 64 || tm == 128 || tm == 256; }
@@ -99,10 +99,16 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
   return launched(moe::launch_permute(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_grouped_ffn_workspace_bytes(int32_t tile_m, int32_t H) {
+  if (!tile_m_ok(tile_m) || H < 1) return 0;
+  return moe::grouped_ffn_ws_bytes(tile_m, H);
+}
+
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, const int32_t* expert_offsets,
                            const int32_t* tiles, const int32_t* num_tiles, const void* w0, const void* w0_up,
                            const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act, int32_t tile_m,
-                           int64_t R_cap, int64_t tiles_cap, void* act_buf, float* y_perm, void* stream) {
+                           int64_t R_cap, int64_t tiles_cap, void* act_buf, float* y_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (E_loc < 1 || H < 1 || F < 1 || R_cap < 0 || tiles_cap < 0) return MOE_ERR_INVALID_ARG;
   if (act != MOE_ACT_GELU && act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
   if ((act == MOE_ACT_SWIGLU) != (w0_up != nullptr)) return MOE_ERR_INVALID_ARG;
@@ -113,6 +119,10 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, con
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (w0_up && !aligned16(w0_up)) return MOE_ERR_INVALID_ARG;
+  if (ws) {
+    if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe::grouped_ffn_ws_bytes(tile_m, H)) return MOE_ERR_WORKSPACE;
+  }
   moe::FfnArgs a;
   a.x_perm = static_cast<const uint16_t*>(x_perm);
   a.counts = expert_counts;
@@ -131,6 +141,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, con
   a.tiles_cap = tiles_cap;
   a.act_buf = static_cast<uint16_t*>(act_buf);
   a.y_perm = y_perm;
+  a.ws = ws;
   a.stream = static_cast<hipStream_t>(stream);
   return launched(moe::launch_grouped_ffn(a));
 }

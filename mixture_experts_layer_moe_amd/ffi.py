@@ -35,11 +35,12 @@ _SIGNATURES = {
     "moe_rows_capacity": (_i64, [_i64, _i32, _i32, _i32]),
     "moe_tiles_capacity": (_i64, [_i64, _i32, _i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_grouped_ffn_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
     "moe_permute": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_grouped_ffn": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                       _i64, _i64, _p, _p, _p]),
+                                       _i64, _i64, _p, _p, _p, _sz, _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i64, _p, _p]),
 }
 
@@ -104,6 +105,10 @@ def tiles_capacity(T: int, k: int, E_loc: int, tile_m: int) -> int:
 
 def permute_workspace_bytes(T: int, k: int, E_loc: int, num_ranks: int) -> int:
     return int(lib().moe_permute_workspace_bytes(T, k, E_loc, num_ranks))
+
+
+def grouped_ffn_workspace_bytes(tile_m: int, H: int) -> int:
+    return int(lib().moe_grouped_ffn_workspace_bytes(tile_m, H))
 
 
 # ---------------------------------------------------------------------------
@@ -177,7 +182,8 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, src_rank: Optional[torc
 
 def moe_grouped_ffn(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor], w1: torch.Tensor,
                     act: str, act_buf: Optional[torch.Tensor] = None,
-                    y_perm: Optional[torch.Tensor] = None, stream=None):
+                    y_perm: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                    stream=None, use_workspace: bool = True):
     _need(w0, torch.bfloat16, "w0")
     _need(w1, torch.bfloat16, "w1")
     if w0_up is not None:
@@ -188,10 +194,13 @@ def moe_grouped_ffn(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor]
         act_buf = torch.empty((p.R_cap, F), dtype=torch.bfloat16, device=dev)
     if y_perm is None:
         y_perm = torch.empty((p.R_cap, H), dtype=torch.float32, device=dev)
+    if ws is None and use_workspace:
+        nbytes = grouped_ffn_workspace_bytes(p.tile_m, H)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(p.x_perm), _ptr(p.expert_counts), _ptr(p.expert_offsets), _ptr(p.tiles), _ptr(p.num_tiles),
         _ptr(w0), _ptr(w0_up), _ptr(w1), E_loc, H, F, ACTS[act], p.tile_m, p.R_cap, p.tiles_cap,
-        _ptr(act_buf), _ptr(y_perm), _stream(stream)))
+        _ptr(act_buf), _ptr(y_perm), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return act_buf, y_perm
 
 

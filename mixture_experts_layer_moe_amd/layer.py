@@ -33,6 +33,8 @@ class MoELayer:
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.act_buf = torch.empty((self.perm.R_cap, cfg.F), dtype=torch.bfloat16, device=dev)
         self.y_perm = torch.empty((self.perm.R_cap, H), dtype=torch.float32, device=dev)
+        ffn_bytes = ffi.grouped_ffn_workspace_bytes(self.tile_m, H)
+        self.ffn_ws = torch.empty(ffn_bytes, dtype=torch.uint8, device=dev) if ffn_bytes else None
         self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     @classmethod
@@ -50,7 +52,7 @@ class MoELayer:
 
     def ffn(self, stream=None):
         ffi.moe_grouped_ffn(self.perm, self.w0, self.w0_up, self.w1, self.cfg.act,
-                            self.act_buf, self.y_perm, stream)
+                            self.act_buf, self.y_perm, self.ffn_ws, stream, use_workspace=False)
 
     def combine(self, stream=None):
         ffi.moe_combine(self.y_perm, self.perm.inv_perm, self.topk_w, self.out, stream)

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_LAUNCH"), (99, b"MOE_ERR_UNKNOWN")]:
         assert L.moe_status_str(code) == name
@@ -106,11 +106,11 @@ def test_permute_validation(L):
 
 def ffn_call(L, **over):
     a = dict(xp=FAKE, cnt=FAKE, off=FAKE, tiles=FAKE, nt=FAKE, w0=FAKE, w0u=FAKE, w1=FAKE, El=8, H=512,
-             F=1024, act=1, tm=64, Rcap=1000, tcap=20, ab=FAKE, y=FAKE)
+             F=1024, act=1, tm=64, Rcap=1000, tcap=20, ab=FAKE, y=FAKE, ws=NULL, wsb=0)
     a.update(over)
     return L.moe_grouped_ffn(a["xp"], a["cnt"], a["off"], a["tiles"], a["nt"], a["w0"], a["w0u"], a["w1"],
                              a["El"], a["H"], a["F"], a["act"], a["tm"], a["Rcap"], a["tcap"], a["ab"], a["y"],
-                             NULL)
+                             a["ws"], a["wsb"], NULL)
 
 
 def test_grouped_ffn_validation(L):
@@ -122,6 +122,16 @@ def test_grouped_ffn_validation(L):
     assert ffn_call(L, tm=8) == UNSUPPORTED
     assert ffn_call(L, y=NULL) == INVALID
     assert ffn_call(L, Rcap=0) == OK                  # no rows: nothing launched
+    assert ffn_call(L, ws=ctypes.c_void_p(16 * 1024 + 8), wsb=1 << 30) == INVALID   # misaligned workspace
+    assert ffn_call(L, tm=128, ws=FAKE, wsb=1) == WORKSPACE                         # workspace too small
+
+
+def test_grouped_ffn_workspace_bytes(L):
+    assert ffi.grouped_ffn_workspace_bytes(64, 4096) == 0      # small tiles never split K
+    assert ffi.grouped_ffn_workspace_bytes(48, 4096) == 0      # unsupported tile
+    n256 = ffi.grouped_ffn_workspace_bytes(256, 4096)
+    assert n256 > 0 and n256 % (256 * 256 * 4) == 0
+    assert ffi.grouped_ffn_workspace_bytes(128, 4224) % (128 * 128 * 4) == 0
 
 
 def test_combine_validation(L):

@@ -386,3 +386,24 @@ def test_layer_graph_capture_replays_match_eager(dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out.view(torch.int32), eager.view(torch.int32))
+
+
+def test_grouped_ffn_split_k_last_round(dev):
+    # Mixtral shape: 35 row tiles x 16 column blocks = 560 layer1 items on 256 CUs, so the last round's
+    # 48 items are split into K slices (workspace) instead of half-width pieces (no workspace).  Both
+    # must agree to fp32 summation-order noise, and the split path must be bitwise reproducible.
+    cfg = W.CONFIGS["mixtral"]
+    d = W.make_inputs(cfg, dev)
+    layer = MoELayer.from_inputs(cfg, d)
+    layer.route()
+    layer.permute()
+    a1, y1 = ffi.moe_grouped_ffn(layer.perm, d["w0"], d["w0_up"], d["w1"], cfg.act, use_workspace=False)
+    a2, y2 = ffi.moe_grouped_ffn(layer.perm, d["w0"], d["w0_up"], d["w1"], cfg.act)
+    a3, y3 = ffi.moe_grouped_ffn(layer.perm, d["w0"], d["w0_up"], d["w1"], cfg.act)
+    torch.cuda.synchronize()
+    real = (layer.perm.row_src >= 0).nonzero().squeeze(1)
+    assert torch.equal(bits16(a1[real]), bits16(a2[real]))
+    y1r, y2r, y3r = y1[real], y2[real], y3[real]
+    assert torch.equal(y2r.view(torch.int32), y3r.view(torch.int32))
+    scale = y1r.abs().max().item()
+    assert (y2r - y1r).abs().max().item() <= 1e-5 * scale
