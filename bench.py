@@ -39,6 +39,12 @@ WORKLOAD_NAMES = {
                     "SwiGLU, Zipf(1.1)-biased router)",
     "ep_share": "expert-parallel share (16384 tokens from 8 source ranks, 8 local of 64 experts, "
                 "top-8, hidden 4096, FFN 2048, SwiGLU)",
+    "tp2_share": "tensor-parallel rank 0 of 2 of the expert-parallel share (FFN columns 0..1023 of "
+                 "8 local experts; partial output)",
+    "tp4_share": "tensor-parallel rank 0 of 4 of the expert-parallel share (FFN columns 0..511 of "
+                 "8 local experts; partial output)",
+    "tp8_share": "tensor-parallel rank 0 of 8 of the expert-parallel share (FFN columns 0..255 of "
+                 "8 local experts; partial output)",
     "decode": "decode-sized MoE layer (64 tokens, hidden 7168, FFN 2048, 256 experts top-8, SwiGLU)",
 }
 
@@ -156,6 +162,41 @@ def cpu_baseline(cfg, d, seconds):
     }
 
 
+def copy_and_cold(layer, stream, iters: int = 10):
+    """HBM context for the two memory-bound calls, measured outside the timed steps.
+
+    copy_GBps: a plain 1 GiB device-to-device copy (bytes read + written per second).
+    permute/combine cold: each call timed alone right after writing a 512 MiB
+    scratch buffer, which evicts its inputs from the 256 MiB last-level cache.
+    """
+    import torch
+    dev = layer.out.device
+    src = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    cold = {}
+    for name, call in (("permute", layer.permute), ("combine", layer.combine)):
+        ms = []
+        for i in range(iters):
+            scratch.fill_(i & 0xFF)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        cold[name] = sorted(ms)[len(ms) // 2]
+    return copy_gbps, cold
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -225,7 +266,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": cfg.T, "hidden": cfg.H,
-                   "ffn": cfg.F, "experts": cfg.E, "local_experts": cfg.n_local, "top_k": cfg.k,
+                   "ffn": cfg.F, "ffn_here": cfg.F_loc, "tp": cfg.tp, "experts": cfg.E,
+                   "local_experts": cfg.n_local, "top_k": cfg.k,
                    "activation": cfg.act, "tile_m": layer.tile_m, "routed_rows": R},
         "tokens_per_s": round(cfg.T / (ms_step * 1e-3), 1),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -243,6 +285,12 @@ def main():
         },
         "cpu_baseline": None,
     }
+    copy_gbps, cold = copy_and_cold(layer, stream)
+    result["copy_GBps"] = round(copy_gbps, 1)
+    result["permute_GBps_cold"] = round(permute_bytes / (cold["permute"] * 1e-3) / 1e9, 1)
+    result["combine_GBps_cold"] = round(combine_bytes / (cold["combine"] * 1e-3) / 1e9, 1)
+    result["pct_of_copy"] = {k: round(100.0 * result[k] / copy_gbps, 1)
+                             for k in ("permute_GBps", "combine_GBps", "permute_GBps_cold", "combine_GBps_cold")}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
     print(json.dumps(result), flush=True)

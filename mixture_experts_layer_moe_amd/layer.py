@@ -31,7 +31,7 @@ class MoELayer:
         self.perm = ffi.alloc_permuted(T, H, k, El, self.tile_m, dev)
         nbytes = ffi.permute_workspace_bytes(T, k, El, cfg.num_ranks)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-        self.act_buf = torch.empty((self.perm.R_cap, cfg.F), dtype=torch.bfloat16, device=dev)
+        self.act_buf = torch.empty((self.perm.R_cap, cfg.F_loc), dtype=torch.bfloat16, device=dev)
         self.y_perm = torch.empty((self.perm.R_cap, H), dtype=torch.float32, device=dev)
         ffn_bytes = ffi.grouped_ffn_workspace_bytes(self.tile_m, H)
         self.ffn_ws = torch.empty(ffn_bytes, dtype=torch.uint8, device=dev) if ffn_bytes else None

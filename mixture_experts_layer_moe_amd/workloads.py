@@ -186,7 +186,10 @@ class MoEConfig:
     FFN width F; act is "swiglu" (three matrices per expert) or "gelu" (two).
     num_ranks > 1 tags every token with a source-rank label in [0, num_ranks)
     (rank 0 = this GPU).  tile_m is the row-tile the reorganised tensors are
-    padded to.
+    padded to.  tp > 1 makes this GPU one tensor-parallel rank (tp_rank) of
+    the layer: it holds FFN columns [tp_rank * F / tp, (tp_rank + 1) * F / tp)
+    of every local expert (F_loc of them) and its output is that slice's
+    partial sum, which a reduce-scatter over the tp ranks would complete.
     """
     name: str
     T: int
@@ -200,6 +203,8 @@ class MoEConfig:
     expert_begin: int = 0
     E_loc: Optional[int] = None
     num_ranks: int = 1
+    tp: int = 1
+    tp_rank: int = 0
     zipf_s: float = 1.1
     w_std: float = 0.02
     seed: int = 0
@@ -208,6 +213,12 @@ class MoEConfig:
     @property
     def n_local(self) -> int:
         return self.E if self.E_loc is None else self.E_loc
+
+    @property
+    def F_loc(self) -> int:
+        """FFN columns per expert held here (F / tp)."""
+        assert self.F % self.tp == 0 and 0 <= self.tp_rank < self.tp, (self.F, self.tp, self.tp_rank)
+        return self.F // self.tp
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -232,6 +243,21 @@ CONFIGS: Dict[str, MoEConfig] = {
         tile_m=256, expert_begin=0, E_loc=8, num_ranks=8,
         description="expert-parallel share: 16384 tokens with source ranks 0..7, experts 0..7 "
                     "of a 64-expert top-8 router, hidden 4096, FFN 2048, SwiGLU"),
+    "tp2_share": MoEConfig(
+        "tp2_share", T=16384, H=4096, F=2048, E=64, k=8, act="swiglu", logits="normal",
+        tile_m=256, expert_begin=0, E_loc=8, num_ranks=8, tp=2,
+        description="tensor-parallel rank 0 of 2 of the expert-parallel share: FFN columns "
+                    "0..1023 of each local expert, partial output"),
+    "tp4_share": MoEConfig(
+        "tp4_share", T=16384, H=4096, F=2048, E=64, k=8, act="swiglu", logits="normal",
+        tile_m=256, expert_begin=0, E_loc=8, num_ranks=8, tp=4,
+        description="tensor-parallel rank 0 of 4 of the expert-parallel share: FFN columns "
+                    "0..511 of each local expert, partial output"),
+    "tp8_share": MoEConfig(
+        "tp8_share", T=16384, H=4096, F=2048, E=64, k=8, act="swiglu", logits="normal",
+        tile_m=256, expert_begin=0, E_loc=8, num_ranks=8, tp=8,
+        description="tensor-parallel rank 0 of 8 of the expert-parallel share: FFN columns "
+                    "0..255 of each local expert, partial output"),
     "decode": MoEConfig(
         "decode", T=64, H=7168, F=2048, E=256, k=8, act="swiglu", logits="normal", tile_m=16,
         description="decode-sized layer: 64 tokens, hidden 7168, FFN 2048, SwiGLU, "
@@ -281,25 +307,31 @@ def make_src_rank(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:
 def expert_weights(cfg: MoEConfig, local_expert: int, device="cpu"):
     """(w0, w0_up, w1) of one local expert as bf16 tensors.
 
-    w0 = W_gate^T or W1^T  [F, H];  w0_up = W_up^T [F, H] or None;
-    w1 = W_down^T or W2^T  [H, F].  The expert's global id keys the generator,
-    so a local range sees the same weights as the full layer.
+    w0 = W_gate^T or W1^T  [F_loc, H];  w0_up = W_up^T [F_loc, H] or None;
+    w1 = W_down^T or W2^T  [H, F_loc].  The expert's global id keys the
+    generator, so a local range sees the same weights as the full layer, and a
+    tensor-parallel rank gets its column slice of the full expert's weights.
     """
     e = cfg.expert_begin + local_expert
     w0 = normal_tensor((cfg.F, cfg.H), cfg.w_std, cfg.seed, TID_W0, e, device)
     w0u = (normal_tensor((cfg.F, cfg.H), cfg.w_std, cfg.seed, TID_W0_UP, e, device)
            if cfg.act == "swiglu" else None)
     w1 = normal_tensor((cfg.H, cfg.F), cfg.w_std, cfg.seed, TID_W1, e, device)
+    if cfg.tp > 1:
+        c0, c1 = cfg.tp_rank * cfg.F_loc, (cfg.tp_rank + 1) * cfg.F_loc
+        w0 = w0[c0:c1].contiguous()
+        w0u = None if w0u is None else w0u[c0:c1].contiguous()
+        w1 = w1[:, c0:c1].contiguous()
     return w0, w0u, w1
 
 
 def make_weights(cfg: MoEConfig, device="cpu"):
     """Stacked per-expert weights (w0 [E_loc,F,H], w0_up [E_loc,F,H] | None, w1 [E_loc,H,F])."""
     El = cfg.n_local
-    w0 = torch.empty((El, cfg.F, cfg.H), dtype=torch.bfloat16, device=device)
-    w0u = (torch.empty((El, cfg.F, cfg.H), dtype=torch.bfloat16, device=device)
+    w0 = torch.empty((El, cfg.F_loc, cfg.H), dtype=torch.bfloat16, device=device)
+    w0u = (torch.empty((El, cfg.F_loc, cfg.H), dtype=torch.bfloat16, device=device)
            if cfg.act == "swiglu" else None)
-    w1 = torch.empty((El, cfg.H, cfg.F), dtype=torch.bfloat16, device=device)
+    w1 = torch.empty((El, cfg.H, cfg.F_loc), dtype=torch.bfloat16, device=device)
     for le in range(El):
         a, b, c = expert_weights(cfg, le, device)
         w0[le].copy_(a)
@@ -324,4 +356,4 @@ def make_inputs(cfg: MoEConfig, device="cpu", weights: bool = True) -> dict:
 def flops(cfg: MoEConfig, R: int) -> int:
     """Algorithmic FLOPs of the two grouped GEMMs for R routed (token, expert) rows."""
     n_mats = 3 if cfg.act == "swiglu" else 2
-    return 2 * R * cfg.H * cfg.F * n_mats
+    return 2 * R * cfg.H * cfg.F_loc * n_mats

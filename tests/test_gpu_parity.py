@@ -205,7 +205,7 @@ def check_grouped_ffn(cfg, tile_m, dev, max_rows=None):
     d = W.make_inputs(cfg, dev)
     idx, _ = P.oracle_route(d["logits"], cfg.k)
     ref, perm = host_reorganised(cfg, d["x"], idx, d["src_rank"], tile_m, dev)
-    act_buf = torch.full((perm.R_cap, cfg.F), -7.0, dtype=torch.bfloat16, device=dev)
+    act_buf = torch.full((perm.R_cap, cfg.F_loc), -7.0, dtype=torch.bfloat16, device=dev)
     y_perm = torch.full((perm.R_cap, cfg.H), -7.0, dtype=torch.float32, device=dev)
     ffi.moe_grouped_ffn(perm, d["w0"], d["w0_up"], d["w1"], cfg.act, act_buf, y_perm)
     torch.cuda.synchronize()
@@ -221,7 +221,7 @@ def check_grouped_ffn(cfg, tile_m, dev, max_rows=None):
     wh = P.HostWeights(d["w0"], d["w0_up"], d["w1"])
     le_of = np.searchsorted(ref["offsets"], rows, side="right") - 1
     y_ref = np.zeros((len(rows), cfg.H))
-    a_ref = np.zeros((len(rows), cfg.F))
+    a_ref = np.zeros((len(rows), cfg.F_loc))
     cache = {}
     for i, (r, le) in enumerate(zip(rows, le_of)):
         if le not in cache:
@@ -386,6 +386,31 @@ def test_layer_graph_capture_replays_match_eager(dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out.view(torch.int32), eager.view(torch.int32))
+
+
+def test_tensor_parallel_partials_sum_to_full_layer(dev):
+    # Each tensor-parallel rank computes its FFN column slice of every local expert; the partial
+    # outputs over all ranks sum to the full layer's output.  The activations of a slice are
+    # bitwise those of the full layer's columns (same rows, same K order), so the sum differs from
+    # the full output only by the fp32 order of layer1's F reduction.
+    cfg = W.CONFIGS["ep_share"].with_(T=1024, H=256, F=512, tile_m=64)
+    full = MoELayer.from_inputs(cfg, W.make_inputs(cfg, dev))
+    full.run()
+    parts = []
+    for r in range(4):
+        c = cfg.with_(tp=4, tp_rank=r)
+        lay = MoELayer.from_inputs(c, W.make_inputs(c, dev))
+        lay.run()
+        torch.cuda.synchronize()
+        cols = slice(r * c.F_loc, (r + 1) * c.F_loc)
+        real = (lay.perm.row_src >= 0).nonzero().squeeze(1)
+        assert torch.equal(bits16(lay.act_buf[real]), bits16(full.act_buf[real][:, cols]))
+        parts.append(lay.out.clone())
+    torch.cuda.synchronize()
+    f = full.out
+    err = (sum(parts) - f).abs().max().item()
+    print(f"[parity] tp=4 partial sum vs full layer: max |err| {err:.3e}, max |out| {f.abs().max().item():.3e}")
+    assert err <= 1e-5 * f.abs().max().item()
 
 
 def test_grouped_ffn_split_k_last_round(dev):

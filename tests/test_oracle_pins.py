@@ -337,3 +337,29 @@ def test_expert_major_layer_matches_dense_mixture(act):
     ref = dense_mixture(X, L, k, ws[1:5], act, expert_begin=1, E_loc=4)[tokens]
     assert np.allclose(out, ref, rtol=1e-11, atol=1e-12)
     assert len(calls) == len(set(calls))          # each expert's weights fetched at most once
+
+
+@pytest.mark.parametrize("act,base", [("swiglu", "ep_share"), ("gelu", "tiny")])
+def test_tensor_parallel_partials_sum_to_full_layer(act, base):
+    # Tensor parallelism over the FFN width (section 2.1): the activation is elementwise over F, so
+    # the partial outputs of disjoint column slices of every expert sum to the full layer.  Weights
+    # come from the workload generator, whose TP ranks slice the full experts' weights.
+    from mixture_experts_layer_moe_amd import workloads as W
+    cfg = W.CONFIGS[base].with_(T=24, H=32, F=64, tile_m=16)
+    assert cfg.act == act
+    d = W.make_inputs(cfg, weights=False)
+    X = d["x"].to(torch.float64).numpy()
+    L = d["logits"].numpy()
+
+    def weights_of(c):
+        w0, w0u, w1 = W.make_weights(c)
+        f = lambda t: None if t is None else t.to(torch.float64).numpy()
+        return [(f(w0[le]), None if w0u is None else f(w0u[le]), f(w1[le])) for le in range(c.n_local)]
+
+    full = O.moe_layer(X, L, cfg.k, weights_of(cfg), act, cfg.expert_begin, cfg.n_local)
+    for tp in (2, 4):
+        parts = [O.moe_layer(X, L, cfg.k, weights_of(cfg.with_(tp=tp, tp_rank=r)), act, cfg.expert_begin,
+                             cfg.n_local) for r in range(tp)]
+        assert all(p.shape == full.shape for p in parts)
+        assert np.allclose(sum(parts), full, rtol=1e-12, atol=1e-12)
+        assert not np.allclose(parts[0], full, rtol=1e-3, atol=1e-6)   # a slice alone is not the layer

@@ -75,7 +75,8 @@ def test_config_shapes_small(name):
     else:
         assert d["src_rank"] is None
     w0, w0u, w1 = W.expert_weights(cfg.with_(H=64, F=128), 0)
-    assert w0.shape == (128, 64) and w1.shape == (64, 128)
+    f_here = 128 // cfg.tp
+    assert w0.shape == (f_here, 64) and w1.shape == (64, f_here)
     assert (w0u is None) == (cfg.act == "gelu")
 
 
@@ -84,3 +85,17 @@ def test_local_range_sees_global_weights():
     a = W.expert_weights(cfg.with_(expert_begin=8), 0)[0]
     b = W.expert_weights(cfg.with_(expert_begin=0, E_loc=64), 8)[0]
     assert torch.equal(a, b)
+
+
+def test_tensor_parallel_rank_slices_full_expert_weights():
+    cfg = W.CONFIGS["ep_share"].with_(T=8, H=32, F=64, tile_m=16)
+    full = W.expert_weights(cfg, 3)
+    for tp in (2, 4):
+        for r in range(tp):
+            c = cfg.with_(tp=tp, tp_rank=r)
+            assert c.F_loc == 64 // tp
+            w0, w0u, w1 = W.expert_weights(c, 3)
+            cols = slice(r * c.F_loc, (r + 1) * c.F_loc)
+            assert torch.equal(w0, full[0][cols]) and torch.equal(w0u, full[1][cols])
+            assert torch.equal(w1, full[2][:, cols]) and w1.is_contiguous()
+    assert W.flops(cfg.with_(tp=4), 100) * 4 == W.flops(cfg, 100)
