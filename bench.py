@@ -220,27 +220,29 @@ def main():
     layer = MoELayer.from_inputs(cfg, d)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        layer.run()
-    torch.cuda.synchronize()
-
-    calls = [layer.route, layer.permute, layer.ffn, layer.combine]
     names = ["route", "permute", "grouped_ffn", "combine"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        for i, c in enumerate(calls):
-            ev[s][i].record(stream)
-            c()
-        ev[s][len(calls)].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
 
-    ms_step = start.elapsed_time(end) / args.steps
-    per_call = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-                for i, n in enumerate(names)}
+    def timed_steps(lay):
+        """W warm-up steps, then K timed steps: (ms per step, per-call ms)."""
+        for _ in range(args.warmup):
+            lay.run()
+        calls = [lay.route, lay.permute, lay.ffn, lay.combine]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(args.steps):
+            for i, c in enumerate(calls):
+                ev[s][i].record(stream)
+                c()
+            ev[s][len(calls)].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return (start.elapsed_time(end) / args.steps,
+                {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                 for i, n in enumerate(names)})
+
+    ms_step, per_call = timed_steps(layer)
 
     # algorithmic work of this batch
     R = int(layer.perm.expert_counts.sum().item())
@@ -285,6 +287,13 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # The same steps with the permutation fused into layer0's operand load (index-only permute,
+    # moe_grouped_ffn_gather), measured after the main line on its own layer buffers.
+    gl = MoELayer.from_inputs(cfg, d, fused_gather=True)
+    g_ms, g_calls = timed_steps(gl)
+    result["fused_gather"] = {"ms_per_step": round(g_ms, 5), "value": round(flop / (g_ms * 1e-3) / 1e12, 3),
+                              "per_call_ms": {n: round(v, 5) for n, v in g_calls.items()}}
+    del gl
     copy_gbps, cold = copy_and_cold(layer, stream)
     result["copy_GBps"] = round(copy_gbps, 1)
     result["permute_GBps_cold"] = round(permute_bytes / (cold["permute"] * 1e-3) / 1e9, 1)

@@ -12,6 +12,8 @@
  *   moe_route_topk   top-k routing and gate weights
  *   moe_permute      reorganisation into expert-contiguous, tile-aligned rows
  *   moe_grouped_ffn  layer0 grouped GEMM + activation, layer1 grouped GEMM
+ *                    (moe_grouped_ffn_gather: the same, with layer0's token
+ *                    rows gathered from x instead of read from x_perm)
  *   moe_combine      top-k weighted reduce back to token order
  *
  * Conventions shared by every call
@@ -119,6 +121,8 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
  * Inputs: x [T, H] bf16; topk_idx [T, k] int32 (from moe_route_topk, or any
  * ids in [0, E) with no repeat within a row); src_rank [T] int32 with values
  * in [0, num_ranks), or NULL = every token is local (rank 0).
+ * x and x_perm may both be NULL: then only the index outputs are written, for
+ * moe_grouped_ffn_gather, which reads the token rows from x itself.
  * ws / ws_bytes: device scratch of at least moe_permute_workspace_bytes().
  * Requires H % 8 == 0, tile_m in {16, 32, 64, 128, 256},
  * E_loc * num_ranks <= 4096, num_ranks <= 64, k <= 32.
@@ -166,6 +170,25 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
                            int32_t tile_m, int64_t R_cap, int64_t tiles_cap,
                            void* act_buf, float* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * moe_grouped_ffn_gather -- moe_grouped_ffn with the permutation fused into
+ * layer0's operand load (section 4: the MoE GEMMs locate their token rows
+ * through an index instead of a materialised permuted copy).  Layer0 reads
+ * row p of its operand as x[row_src[p] / k] straight from the token matrix
+ * x [T, H] bf16 (padding rows, row_src[p] < 0, read as zeros and are never
+ * stored), so moe_permute can run with x = x_perm = NULL.  row_src [R_cap]
+ * int32, T and k are those of the moe_permute call that produced row_src;
+ * every other argument, the outputs and the errors are as for
+ * moe_grouped_ffn.  Also requires T * H * 2 <= 2^31 - 1.
+ */
+moe_status moe_grouped_ffn_gather(const void* x, const int32_t* row_src, int64_t T, int32_t k,
+                                  const int32_t* expert_counts, const int32_t* expert_offsets,
+                                  const int32_t* tiles, const int32_t* num_tiles, const void* w0,
+                                  const void* w0_up, const void* w1, int32_t E_loc, int32_t H,
+                                  int32_t F, int32_t act, int32_t tile_m, int64_t R_cap,
+                                  int64_t tiles_cap, void* act_buf, float* y_perm, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- gather and top-k reduce (section 2.1: expert outputs are

@@ -50,6 +50,11 @@ struct FfnArgs {
   uint16_t* act_buf;
   float* y_perm;
   void* ws;  // split-K partials of layer1's last round, or null
+  // x_perm == null: layer0 gathers its rows from x [T, H] through row_src (t * topk + slot; < 0 padding)
+  const uint16_t* x;
+  const int32_t* row_src;
+  int topk;
+  int64_t T;
   hipStream_t stream;
 };
 size_t grouped_ffn_ws_bytes(int tile_m, int H);

@@ -203,12 +203,16 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 // compiler starts matching LDS reads against the direct-to-LDS loads still in
 // flight and inserts full vmcnt(0) drains inside the K loop.  The ring is
 // synchronised by the explicit waits below instead.
-template <int BM, int BN, bool DUAL, int EPI, int STAGES>
+//
+// GATHER: A is the token matrix x [T, K] itself and padded row p of the tile
+// reads token row_src[p] / topk (row_src < 0: padding, read as zeros) -- the
+// layer0 operand gathered on the fly instead of from a permuted copy.
+template <int BM, int BN, bool DUAL, int EPI, int STAGES, bool GATHER>
 __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
                                           int N, int K, int le, int row0, int valid, int n0, int k_begin, int k_len,
                                           void* __restrict__ C, int64_t c_row0, int ldc, int c_n0, int wave,
-                                          int lane) {
+                                          int lane, const int32_t* __restrict__ row_src, int topk, int64_t T) {
   constexpr int NWAVES = 4, WN = 2;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BROWS = NMAT * BN;               // weight rows staged per stage
@@ -228,12 +232,23 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   // out-of-range reads return zeros).  A and B share the row stride K, so one
   // per-lane byte offset serves every direct-to-LDS load of this wave:
   // row (q * NWAVES + wave) * 8 + lane / 8, logical chunk swizzled for that row.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
+  const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, T * K * 2) : make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
   const __amdgpu_buffer_rsrc_t rb1 = DUAL ? make_rsrc(B1 + le * b_expert + (int64_t)n0 * K, BN * K * 2) : rb0;
   const __amdgpu_buffer_rsrc_t rnone = make_rsrc(A, 0);  // no records: every load reads zero, fetches nothing
   const int r_in = lane >> 3;
   const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
+  // GATHER: per A load, this lane's byte offset into x (its token row, same
+  // swizzled chunk); out of range for padding rows, which then read zeros.
+  uint32_t voff_a[GATHER ? A_PIECES : 1];
+  if (GATHER) {
+#pragma unroll
+    for (int q = 0; q < A_PIECES; ++q) {
+      const int src = row_src[row0 + (q * NWAVES + wave) * 8 + r_in];
+      const int64_t t = src >= 0 ? src / topk : -1;
+      voff_a[q] = (t >= 0 && t < T) ? (uint32_t)((t * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2) : 0x80000000u;
+    }
+  }
   floatx16 acc[NMAT][TN][TM];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
@@ -244,17 +259,20 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][j][i][v] = 0.f;
   // Direct-to-LDS load number p (0 <= p < LOADS, a constant after unrolling)
-  // of stage buffer `stage` for K offset k0, through the resources (a, b0, b1):
-  // the first A_PIECES stage 8 * NWAVES token rows each, the rest the rows of
-  // the weight matrices.
+  // of stage buffer `stage` for K offset k0, through the resources (a, b0, b1)
+  // and this lane's byte offset vo (MOE_VOFF(p)): the first A_PIECES stage
+  // 8 * NWAVES token rows each, the rest the rows of the weight matrices.
   auto load = [&](int p, int stage, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0,
-                  __amdgpu_buffer_rsrc_t b1) {
+                  __amdgpu_buffer_rsrc_t b1, uint32_t vo) {
     const bool is_a = p < A_PIECES;
     const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
     const int lds_off = (is_a ? 0 : A_BYTES + m * BN * 128) + (q * NWAVES + wave) * 1024;
+    const bool g = GATHER && is_a;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a : (m ? b1 : b0), (lds_void*)(smem + stage * STAGE + lds_off), 16,
-                                             voff, (q * 8 * NWAVES * K + k_begin + k0) * 2, 0, 0);
+                                             vo, ((g ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0, 0);
   };
+// Byte offset of this lane for load p: its gathered token row for an A load, else the shared one.
+#define MOE_VOFF(p) (GATHER && (p) < A_PIECES ? voff_a[GATHER && (p) < A_PIECES ? (p) : 0] : voff)
   struct Frags {
     bf16x8 a[TM];
     bf16x8 b[NMAT][TN];
@@ -313,7 +331,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   for (int st = 0; st + 1 < STAGES; ++st)
     if (st < nk)
 #pragma unroll
-      for (int p = 0; p < LOADS; ++p) load(p, st, st * BK, ra, rb0, rb1);
+      for (int p = 0; p < LOADS; ++p) load(p, st, st * BK, ra, rb0, rb1, MOE_VOFF(p));
   {  // stage 0 has landed once only the prologue's later stages are in flight
     const int later = (nk < STAGES - 1 ? nk : STAGES - 1) - 1;
     wait_stages<LOADS, STAGES - 2>(later);
@@ -332,7 +350,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   _Pragma("unroll") for (int t = 0; t < NREAD + np_; ++t) {                         \
     const int sl = step_slot(t, NREAD, np_);                                        \
     if (sl >= 0) read_one(nxt, (BUF), ks + 1, sl);                                  \
-    else load(ks * PER_STEP - 1 - sl, (TBUF), (TS) * BK, (RA), (RB0), (RB1));       \
+    else load(ks * PER_STEP - 1 - sl, (TBUF), (TS) * BK, (RA), (RB0), (RB1), MOE_VOFF(ks * PER_STEP - 1 - sl)); \
   }                                                                                 \
   MOE_MFMAS(cur, 0, NMFMA)                                                          \
   /* Keep this step's MFMAs ahead of the loads that follow them (MFMAs have no */   \
@@ -378,6 +396,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
     MOE_MFMAS(cur, 0, NMFMA)
   }
 #undef MOE_INNER_STEPS
+#undef MOE_VOFF
 #undef MOE_MFMAS
 
   // Epilogue: lane holds, for token row m = lane % 32 of each 32-row block,
@@ -431,14 +450,15 @@ __host__ __device__ inline int tail_ksplit(int64_t rem, int G, int nk) {
 //  * otherwise each is split into two half-width pieces.
 // Either way the last round costs a fraction of a full item instead of
 // leaving most CUs idle behind a few full ones.
-template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES, bool SPLITK>
+template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES, bool SPLITK, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const uint16_t* __restrict__ A,    // [R_cap, K] bf16 (x_perm or act)
     const uint16_t* __restrict__ B0,   // [E_loc, N, K] bf16
     const uint16_t* __restrict__ B1,   // [E_loc, N, K] bf16 (DUAL) or null
     int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
-    int64_t R_cap, int E_loc, void* __restrict__ C, float* __restrict__ ws) {
+    int64_t R_cap, int E_loc, void* __restrict__ C, float* __restrict__ ws, const int32_t* __restrict__ row_src,
+    int topk, int64_t T) {
   static_assert(!SPLITK || EPI == EPI_F32, "K slices need a linear epilogue");
   __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN, DUAL>(STAGES)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,16 +487,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
   for (int64_t item = vid; item < full; item += G) {
     int le, row0, valid, n0;
     if (!coords(item, le, row0, valid, n0)) continue;  // block-uniform
-    gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, row0, N, n0, wave,
-                                         lane);
+    gemm_item<BM, BN, DUAL, EPI, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, row0, N, n0,
+                                                 wave, lane, row_src, topk, T);
   }
   if (S > 1) {
     const int k_len = K / S;
     for (int64_t piece = vid; piece < S * (total - full); piece += G) {
       int le, row0, valid, n0;
       if (!coords(full + piece / S, le, row0, valid, n0)) continue;
-      gemm_item<BM, BN, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, n0, (int)(piece % S) * k_len,
-                                           k_len, ws + piece * (int64_t)(BM * BN), 0, BN, 0, wave, lane);
+      gemm_item<BM, BN, DUAL, EPI, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0,
+                                                   (int)(piece % S) * k_len, k_len, ws + piece * (int64_t)(BM * BN), 0,
+                                                   BN, 0, wave, lane, row_src, topk, T);
     }
     return;
   }
@@ -484,8 +505,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     int le, row0, valid, n0;
     if (!coords(full + piece / 2, le, row0, valid, n0)) continue;
     const int nh = n0 + (int)(piece % 2) * (BN / 2);
-    gemm_item<BM, BN / 2, DUAL, EPI, STAGES>(smem, A, B0, B1, N, K, le, row0, valid, nh, 0, K, C, row0, N, nh, wave,
-                                             lane);
+    gemm_item<BM, BN / 2, DUAL, EPI, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, nh, 0, K, C, row0, N,
+                                                     nh, wave, lane, row_src, topk, T);
   }
 }
 
@@ -530,12 +551,12 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // Small-tile kernel (tile_m <= 64): WM x WN waves of v_mfma_f32_16x16x32_bf16,
 // double-buffered LDS.  These shapes stream weights from HBM.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, int ORDER>
+template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, int ORDER, bool GATHER>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
     int N, int K, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
-    int64_t R_cap, int E_loc, void* __restrict__ C) {
+    int64_t R_cap, int E_loc, void* __restrict__ C, const int32_t* __restrict__ row_src, int topk, int64_t T) {
   constexpr int NWAVES = WM * WN;
   constexpr int NMAT = DUAL ? 2 : 1;
   constexpr int BROWS = NMAT * BN;
@@ -545,6 +566,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
   constexpr int TM = WT_M / 16, TN = WT_N / 16;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(BM % 8 == 0 && BROWS % 8 == 0, "rows per stage");
+  static_assert(!GATHER || BM / 8 <= NWAVES, "gathered rows: one 8-row group per wave");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
@@ -581,6 +603,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
     const int n0 = nb * BN;
 
     const uint16_t* a_g = A + (int64_t)row0 * K;
+    // GATHER: this lane's token row of x for its wave's 8-row group of A
+    // (padding rows read token 0: valid memory, never stored).
+    const uint16_t* a_row = A;
+    if (GATHER && wave < BM / 8) {
+      const int src = row_src[row0 + wave * 8 + (lane >> 3)];
+      const int64_t t = src >= 0 ? src / topk : 0;
+      a_row = A + (t < T ? t : 0) * (int64_t)K;
+    }
     const uint16_t* b0_g = B0 + le * b_expert + (int64_t)n0 * K;
     const uint16_t* b1_g = DUAL ? B1 + le * b_expert + (int64_t)n0 * K : nullptr;
 
@@ -594,7 +624,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
 
     auto issue = [&](int stage, int k0) {
       char* s = smem + stage * STAGE;
-      stage_any(a_g + k0, BM, s);
+      if (GATHER) {
+        if (wave < BM / 8)
+          __builtin_amdgcn_global_load_lds(a_row + k0 + ((lane & 7) ^ swz(wave * 8 + (lane >> 3))) * 8,
+                                           (lds_void*)(s + wave * 1024), 16, 0, 0);
+      } else {
+        stage_any(a_g + k0, BM, s);
+      }
       stage_any(b0_g + k0, BN, s + A_BYTES);
       if (DUAL) stage_any(b1_g + k0, BN, s + A_BYTES + BN * 128);
     };
@@ -684,10 +720,10 @@ template <int BM, int BN, int ST>
 hipError_t launch_layer1(const FfnArgs& a) {
   const int64_t max_items = a.tiles_cap * (a.H / BN);
   if (a.ws == nullptr)
-    return launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, false>, 256, max_items, a.act_buf,
-                             a.w1, nullptr, a.H, a.F, a, a.y_perm, (float*)nullptr);
-  hipError_t e = launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, true>, 256, max_items,
-                                   a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, static_cast<float*>(a.ws));
+    return launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, false, false>, 256, max_items,
+                             a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, (float*)nullptr, (const int32_t*)nullptr, 0, (int64_t)0);
+  hipError_t e = launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, true, false>, 256, max_items,
+                                   a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, static_cast<float*>(a.ws), (const int32_t*)nullptr, 0, (int64_t)0);
   if (e != hipSuccess) return e;
   const int G = (int)persistent_grid(max_items);
   hipLaunchKernelGGL((reduce_slices_kernel<BM, BN, ORDER_N>), dim3((unsigned)(G * (BM / 16))), dim3(256), 0, a.stream,
@@ -698,33 +734,44 @@ hipError_t launch_layer1(const FfnArgs& a) {
 
 // tile_m >= 128: layer0 = BM x (BN0 gate + BN0 up) (GELU: BM x BN0), layer1 = BM x BN1
 // (BM x 128 when H is not a multiple of BN1).
+// Layer0 over BM x BN0 items, reading the token rows from x_perm or (GATHER) from x.
+template <int BM, int BN0, int ST0, bool GATHER>
+hipError_t launch_big_layer0(const FfnArgs& a) {
+  const int64_t items = a.tiles_cap * (a.F / BN0);
+  const uint16_t* A = GATHER ? a.x : a.x_perm;
+  if (a.act == MOE_ACT_SWIGLU_I)
+    return launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0, false, GATHER>, 256, items, A,
+                             a.w0, a.w0_up, a.F, a.H, a, a.act_buf, (float*)nullptr, a.row_src, a.topk, a.T);
+  return launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0, false, GATHER>, 256, items, A,
+                           a.w0, nullptr, a.F, a.H, a, a.act_buf, (float*)nullptr, a.row_src, a.topk, a.T);
+}
+
 template <int BM, int BN0, int ST0, int BN1, int ST1>
 hipError_t launch_big(const FfnArgs& a) {
-  hipError_t e;
-  if (a.act == MOE_ACT_SWIGLU_I)
-    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0, false>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, (float*)nullptr);
-  else
-    e = launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0, false>, 256, a.tiles_cap * (a.F / BN0),
-                          a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf, (float*)nullptr);
+  hipError_t e = a.x_perm ? launch_big_layer0<BM, BN0, ST0, false>(a) : launch_big_layer0<BM, BN0, ST0, true>(a);
   if (e != hipSuccess) return e;
   if (a.H % BN1 == 0) return launch_layer1<BM, BN1, ST1>(a);
   return launch_layer1<BM, 128, ST0>(a);
 }
 
 // tile_m <= 64: weight-streaming shapes.
+template <int BM, int BN0, int WM, int WN, bool GATHER>
+hipError_t launch_small_layer0(const FfnArgs& a) {
+  const int64_t items = a.tiles_cap * (a.F / BN0);
+  const uint16_t* A = GATHER ? a.x : a.x_perm;
+  if (a.act == MOE_ACT_SWIGLU_I)
+    return launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, true, EPI_SWIGLU, ORDER_M, GATHER>, WM * WN * 64, items,
+                             A, a.w0, a.w0_up, a.F, a.H, a, a.act_buf, a.row_src, a.topk, a.T);
+  return launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, false, EPI_GELU, ORDER_M, GATHER>, WM * WN * 64, items, A,
+                           a.w0, nullptr, a.F, a.H, a, a.act_buf, a.row_src, a.topk, a.T);
+}
+
 template <int BM, int WM, int WN, int BN0, int BN1, int WM1, int WN1>
 hipError_t launch_small(const FfnArgs& a) {
-  hipError_t e;
-  if (a.act == MOE_ACT_SWIGLU_I)
-    e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, true, EPI_SWIGLU, ORDER_M>, WM * WN * 64,
-                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, a.w0_up, a.F, a.H, a, a.act_buf);
-  else
-    e = launch_persistent(gemm_mfma16_kernel<BM, BN0, WM, WN, false, EPI_GELU, ORDER_M>, WM * WN * 64,
-                          a.tiles_cap * (a.F / BN0), a.x_perm, a.w0, nullptr, a.F, a.H, a, a.act_buf);
+  hipError_t e = a.x_perm ? launch_small_layer0<BM, BN0, WM, WN, false>(a) : launch_small_layer0<BM, BN0, WM, WN, true>(a);
   if (e != hipSuccess) return e;
-  return launch_persistent(gemm_mfma16_kernel<BM, BN1, WM1, WN1, false, EPI_F32, ORDER_N>, WM1 * WN1 * 64,
-                           a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm);
+  return launch_persistent(gemm_mfma16_kernel<BM, BN1, WM1, WN1, false, EPI_F32, ORDER_N, false>, WM1 * WN1 * 64,
+                           a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, (const int32_t*)nullptr, 0, (int64_t)0);
 }
 
 }  // namespace

@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool tile_m_ok(int32_t tm) { return tm == 16 || tm == 32 || tm == 64 || tm == 128 || tm == 256; }
@@ -69,7 +69,10 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
   const int64_t R_cap = moe_rows_capacity(T, k, E_loc, tile_m);
   if (T * (int64_t)k > INT32_MAX || R_cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  const void* ptrs[] = {x, topk_idx, x_perm, expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles, ws};
+  // x and x_perm both null: indices only (the rows are gathered later by moe_grouped_ffn_gather).
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles, ws};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (src_rank && !aligned16(src_rank)) return MOE_ERR_INVALID_ARG;
@@ -104,27 +107,42 @@ size_t moe_grouped_ffn_workspace_bytes(int32_t tile_m, int32_t H) {
   return moe::grouped_ffn_ws_bytes(tile_m, H);
 }
 
-moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, const int32_t* expert_offsets,
-                           const int32_t* tiles, const int32_t* num_tiles, const void* w0, const void* w0_up,
-                           const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act, int32_t tile_m,
-                           int64_t R_cap, int64_t tiles_cap, void* act_buf, float* y_perm, void* ws,
-                           size_t ws_bytes, void* stream) {
+namespace {
+
+// Shared validation and launch of moe_grouped_ffn (x_perm given) and
+// moe_grouped_ffn_gather (x, row_src, T, k given, x_perm null).
+moe_status grouped_ffn_impl(const void* x_perm, const void* x, const int32_t* row_src, int64_t T, int32_t k,
+                            const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* tiles,
+                            const int32_t* num_tiles, const void* w0, const void* w0_up, const void* w1,
+                            int32_t E_loc, int32_t H, int32_t F, int32_t act, int32_t tile_m, int64_t R_cap,
+                            int64_t tiles_cap, void* act_buf, float* y_perm, void* ws, size_t ws_bytes,
+                            void* stream) {
   if (E_loc < 1 || H < 1 || F < 1 || R_cap < 0 || tiles_cap < 0) return MOE_ERR_INVALID_ARG;
   if (act != MOE_ACT_GELU && act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
   if ((act == MOE_ACT_SWIGLU) != (w0_up != nullptr)) return MOE_ERR_INVALID_ARG;
   if (H % 128 != 0 || F % 128 != 0 || !tile_m_ok(tile_m)) return MOE_ERR_UNSUPPORTED;
   if (R_cap > INT32_MAX || tiles_cap > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const bool gather = x_perm == nullptr;
+  if (gather) {
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (T * (int64_t)H * 2 > INT32_MAX || T * (int64_t)k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  }
   if (R_cap == 0 || tiles_cap == 0) return MOE_OK;
-  const void* ptrs[] = {x_perm, expert_counts, expert_offsets, tiles, num_tiles, w0, w1, act_buf, y_perm};
+  const void* ptrs[] = {gather ? x : x_perm, expert_counts, expert_offsets, tiles, num_tiles, w0, w1, act_buf, y_perm};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (gather && (!row_src || !aligned16(row_src))) return MOE_ERR_INVALID_ARG;
   if (w0_up && !aligned16(w0_up)) return MOE_ERR_INVALID_ARG;
   if (ws) {
     if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < moe::grouped_ffn_ws_bytes(tile_m, H)) return MOE_ERR_WORKSPACE;
   }
-  moe::FfnArgs a;
+  moe::FfnArgs a{};
   a.x_perm = static_cast<const uint16_t*>(x_perm);
+  a.x = static_cast<const uint16_t*>(x);
+  a.row_src = row_src;
+  a.topk = k;
+  a.T = T;
   a.counts = expert_counts;
   a.offsets = expert_offsets;
   a.tiles = tiles;
@@ -144,6 +162,29 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, con
   a.ws = ws;
   a.stream = static_cast<hipStream_t>(stream);
   return launched(moe::launch_grouped_ffn(a));
+}
+
+}  // namespace
+
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts, const int32_t* expert_offsets,
+                           const int32_t* tiles, const int32_t* num_tiles, const void* w0, const void* w0_up,
+                           const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act, int32_t tile_m,
+                           int64_t R_cap, int64_t tiles_cap, void* act_buf, float* y_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!x_perm) return MOE_ERR_INVALID_ARG;
+  return grouped_ffn_impl(x_perm, nullptr, nullptr, 0, 0, expert_counts, expert_offsets, tiles, num_tiles, w0, w0_up,
+                          w1, E_loc, H, F, act, tile_m, R_cap, tiles_cap, act_buf, y_perm, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_ffn_gather(const void* x, const int32_t* row_src, int64_t T, int32_t k,
+                                  const int32_t* expert_counts, const int32_t* expert_offsets,
+                                  const int32_t* tiles, const int32_t* num_tiles, const void* w0,
+                                  const void* w0_up, const void* w1, int32_t E_loc, int32_t H, int32_t F,
+                                  int32_t act, int32_t tile_m, int64_t R_cap, int64_t tiles_cap, void* act_buf,
+                                  float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (!x) return MOE_ERR_INVALID_ARG;
+  return grouped_ffn_impl(nullptr, x, row_src, T, k, expert_counts, expert_offsets, tiles, num_tiles, w0, w0_up, w1,
+                          E_loc, H, F, act, tile_m, R_cap, tiles_cap, act_buf, y_perm, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int32_t k,

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     dst[j] = j < k ? __shfl(p, j) : -1;
     any |= dst[j] >= 0;
   }
-  if (!any) return;
+  if (!any || x_perm == nullptr) return;  // no local slot, or indices only
   const int nch = H / 8;  // 16-byte chunks per row
   const intx4* src = x + t * nch;
   constexpr int U = 8;    // up to 8 x 16 B per lane in flight: an 8 KiB row per pass

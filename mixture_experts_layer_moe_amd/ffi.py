@@ -41,6 +41,8 @@ _SIGNATURES = {
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_grouped_ffn": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                        _i64, _i64, _p, _p, _p, _sz, _p]),
+    "moe_grouped_ffn_gather": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
+                                              _i32, _i32, _i64, _i64, _p, _p, _p, _sz, _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i64, _p, _p]),
 }
 
@@ -133,7 +135,7 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True,
 @dataclass
 class Permuted:
     """Outputs of moe_permute (all device tensors; counts stay on the device)."""
-    x_perm: torch.Tensor          # [R_cap, H] bf16
+    x_perm: Optional[torch.Tensor]  # [R_cap, H] bf16, or None for an index-only permute
     expert_counts: torch.Tensor   # [E_loc] int32
     expert_offsets: torch.Tensor  # [E_loc + 1] int32
     row_src: torch.Tensor         # [R_cap] int32
@@ -145,12 +147,13 @@ class Permuted:
     tiles_cap: int
 
 
-def alloc_permuted(T: int, H: int, k: int, E_loc: int, tile_m: int, device) -> Permuted:
+def alloc_permuted(T: int, H: int, k: int, E_loc: int, tile_m: int, device, rows: bool = True) -> Permuted:
+    """Outputs for moe_permute; rows=False leaves out x_perm (index-only permute)."""
     R_cap = rows_capacity(T, k, E_loc, tile_m)
     tcap = tiles_capacity(T, k, E_loc, tile_m)
     i32 = dict(dtype=torch.int32, device=device)
     return Permuted(
-        x_perm=torch.empty((R_cap, H), dtype=torch.bfloat16, device=device),
+        x_perm=torch.empty((R_cap, H), dtype=torch.bfloat16, device=device) if rows else None,
         expert_counts=torch.empty(E_loc, **i32), expert_offsets=torch.empty(E_loc + 1, **i32),
         row_src=torch.empty(R_cap, **i32), inv_perm=torch.empty((T, k), **i32),
         tiles=torch.empty((tcap, 2), **i32), num_tiles=torch.empty(1, **i32),
@@ -160,7 +163,8 @@ def alloc_permuted(T: int, H: int, k: int, E_loc: int, tile_m: int, device) -> P
 def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, src_rank: Optional[torch.Tensor], E: int,
                 expert_begin: int, E_loc: int, num_ranks: int, tile_m: int,
                 out: Optional[Permuted] = None, ws: Optional[torch.Tensor] = None,
-                stream=None) -> Permuted:
+                stream=None, copy_rows: bool = True) -> Permuted:
+    """copy_rows=False writes only the indices (for moe_grouped_ffn_gather)."""
     _need(x, torch.bfloat16, "x")
     _need(topk_idx, torch.int32, "topk_idx")
     if src_rank is not None:
@@ -168,13 +172,15 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, src_rank: Optional[torc
     T, H = x.shape
     k = topk_idx.shape[1]
     if out is None:
-        out = alloc_permuted(T, H, k, E_loc, tile_m, x.device)
+        out = alloc_permuted(T, H, k, E_loc, tile_m, x.device, rows=copy_rows)
+    copy_rows = copy_rows and out.x_perm is not None
     nbytes = permute_workspace_bytes(T, k, E_loc, num_ranks)
     if ws is None:
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     _check("moe_permute", lib().moe_permute(
-        _ptr(x), _ptr(topk_idx), _ptr(src_rank), T, H, k, E, expert_begin, E_loc, num_ranks, tile_m,
-        _ptr(out.x_perm), _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.row_src),
+        _ptr(x) if copy_rows else None, _ptr(topk_idx), _ptr(src_rank), T, H, k, E, expert_begin, E_loc, num_ranks, tile_m,
+        _ptr(out.x_perm) if copy_rows else None, _ptr(out.expert_counts), _ptr(out.expert_offsets),
+        _ptr(out.row_src),
         _ptr(out.inv_perm), _ptr(out.tiles), _ptr(out.num_tiles), _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
@@ -201,6 +207,34 @@ def moe_grouped_ffn(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor]
         _ptr(p.x_perm), _ptr(p.expert_counts), _ptr(p.expert_offsets), _ptr(p.tiles), _ptr(p.num_tiles),
         _ptr(w0), _ptr(w0_up), _ptr(w1), E_loc, H, F, ACTS[act], p.tile_m, p.R_cap, p.tiles_cap,
         _ptr(act_buf), _ptr(y_perm), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return act_buf, y_perm
+
+
+def moe_grouped_ffn_gather(x: torch.Tensor, p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor],
+                           w1: torch.Tensor, act: str, act_buf: Optional[torch.Tensor] = None,
+                           y_perm: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                           stream=None, use_workspace: bool = True):
+    """moe_grouped_ffn with layer0 reading its rows from x through p.row_src (no x_perm needed)."""
+    _need(x, torch.bfloat16, "x")
+    _need(w0, torch.bfloat16, "w0")
+    _need(w1, torch.bfloat16, "w1")
+    if w0_up is not None:
+        _need(w0_up, torch.bfloat16, "w0_up")
+    T, k = p.inv_perm.shape
+    E_loc, F, H = w0.shape
+    dev = w0.device
+    if act_buf is None:
+        act_buf = torch.empty((p.R_cap, F), dtype=torch.bfloat16, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty((p.R_cap, H), dtype=torch.float32, device=dev)
+    if ws is None and use_workspace:
+        nbytes = grouped_ffn_workspace_bytes(p.tile_m, H)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    _check("moe_grouped_ffn_gather", lib().moe_grouped_ffn_gather(
+        _ptr(x), _ptr(p.row_src), T, k, _ptr(p.expert_counts), _ptr(p.expert_offsets), _ptr(p.tiles),
+        _ptr(p.num_tiles), _ptr(w0), _ptr(w0_up), _ptr(w1), E_loc, H, F, ACTS[act], p.tile_m, p.R_cap,
+        p.tiles_cap, _ptr(act_buf), _ptr(y_perm), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
     return act_buf, y_perm
 
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_LAUNCH"), (99, b"MOE_ERR_UNKNOWN")]:
         assert L.moe_status_str(code) == name
@@ -97,7 +97,10 @@ def test_permute_validation(L):
     assert permute_call(L, tm=48) == UNSUPPORTED           # tile size not implemented
     assert permute_call(L, H=500) == UNSUPPORTED           # H % 8
     assert permute_call(L, R=65) == UNSUPPORTED            # too many ranks
-    assert permute_call(L, xp=NULL) == INVALID
+    assert permute_call(L, xp=NULL) == INVALID             # rows copied from x need x_perm
+    assert permute_call(L, x=NULL) == INVALID              # ... and x_perm needs x
+    assert permute_call(L, x=NULL, xp=NULL, rs=NULL) == INVALID   # index-only still needs the indices
+    assert permute_call(L, x=NULL, xp=NULL, T=0) == OK
     assert permute_call(L, ws=ctypes.c_void_p(16 * 1024 + 8)) == INVALID
     need = ffi.permute_workspace_bytes(64, 2, 8, 1)
     assert permute_call(L, wsb=need - 1) == WORKSPACE
@@ -124,6 +127,28 @@ def test_grouped_ffn_validation(L):
     assert ffn_call(L, Rcap=0) == OK                  # no rows: nothing launched
     assert ffn_call(L, ws=ctypes.c_void_p(16 * 1024 + 8), wsb=1 << 30) == INVALID   # misaligned workspace
     assert ffn_call(L, tm=128, ws=FAKE, wsb=1) == WORKSPACE                         # workspace too small
+
+
+def gather_call(L, **over):
+    a = dict(x=FAKE, rs=FAKE, T=4096, k=2, cnt=FAKE, off=FAKE, tiles=FAKE, nt=FAKE, w0=FAKE, w0u=FAKE, w1=FAKE,
+             El=8, H=512, F=1024, act=1, tm=64, Rcap=1000, tcap=20, ab=FAKE, y=FAKE, ws=NULL, wsb=0)
+    a.update(over)
+    return L.moe_grouped_ffn_gather(a["x"], a["rs"], a["T"], a["k"], a["cnt"], a["off"], a["tiles"], a["nt"],
+                                    a["w0"], a["w0u"], a["w1"], a["El"], a["H"], a["F"], a["act"], a["tm"],
+                                    a["Rcap"], a["tcap"], a["ab"], a["y"], a["ws"], a["wsb"], NULL)
+
+
+def test_grouped_ffn_gather_validation(L):
+    assert gather_call(L, x=NULL) == INVALID
+    assert gather_call(L, rs=NULL) == INVALID          # rows come through row_src
+    assert gather_call(L, k=0) == INVALID
+    assert gather_call(L, T=-1) == INVALID
+    assert gather_call(L, T=1 << 20, H=1024) == UNSUPPORTED   # x beyond a 2 GiB buffer resource
+    assert gather_call(L, act=0) == INVALID            # same checks as moe_grouped_ffn
+    assert gather_call(L, H=576) == UNSUPPORTED
+    assert gather_call(L, tm=128, ws=FAKE, wsb=1) == WORKSPACE
+    assert gather_call(L, Rcap=0) == OK
+    assert ffn_call(L, xp=NULL) == INVALID             # the permuted-copy entry point needs x_perm
 
 
 def test_grouped_ffn_workspace_bytes(L):

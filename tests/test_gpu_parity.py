@@ -300,9 +300,9 @@ def test_combine_full_size(dev, name):
 # the whole layer through the four calls
 # ---------------------------------------------------------------------------
 
-def run_layer(cfg, dev, tile_m=None):
+def run_layer(cfg, dev, tile_m=None, fused_gather=False):
     d = W.make_inputs(cfg, dev)
-    layer = MoELayer.from_inputs(cfg, d, tile_m=tile_m)
+    layer = MoELayer.from_inputs(cfg, d, tile_m=tile_m, fused_gather=fused_gather)
     out = layer.run()
     torch.cuda.synchronize()
     return d, layer, out
@@ -328,15 +328,39 @@ SMALL_LAYERS = {
 }
 
 
+@pytest.mark.parametrize("fused_gather", [False, True], ids=["x_perm", "gather"])
 @pytest.mark.parametrize("name", list(SMALL_LAYERS))
-def test_layer_small_full_check(dev, name):
+def test_layer_small_full_check(dev, name, fused_gather):
     cfg = SMALL_LAYERS[name]
-    d, layer, out = run_layer(cfg, dev)
+    d, layer, out = run_layer(cfg, dev, fused_gather=fused_gather)
     idx, w = check_layer_routing_and_permutation(cfg, d, layer)
     wh = P.HostWeights(d["w0"], d["w0_up"], d["w1"])
     ref = O.moe_layer_expert_major(P.to_np64(d["x"]), cfg.k, wh, cfg.act, (idx, w), list(range(cfg.T)),
                                    cfg.expert_begin, cfg.n_local)
-    P.assert_output_close(out.cpu().double().numpy(), ref, name)
+    P.assert_output_close(out.cpu().double().numpy(), ref, name + (" (fused gather)" if fused_gather else ""))
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_fused_gather_matches_permuted_copy(dev, name):
+    # Layer0 reading its rows from x through row_src (index-only permute, no x_perm) must give the
+    # same activation, layer1 output and layer output, bit for bit, as reading the permuted copy: the
+    # operand values and the accumulation order are the same.
+    cfg = W.CONFIGS[name]
+    d = W.make_inputs(cfg, dev)
+    a = MoELayer.from_inputs(cfg, d)
+    b = MoELayer.from_inputs(cfg, d, fused_gather=True)
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    assert b.perm.x_perm is None
+    for t in ("expert_counts", "expert_offsets", "row_src", "inv_perm", "num_tiles"):
+        assert torch.equal(getattr(a.perm, t), getattr(b.perm, t)), t
+    nt = int(a.perm.num_tiles.item())
+    assert torch.equal(a.perm.tiles[:nt], b.perm.tiles[:nt])
+    real = (a.perm.row_src >= 0).nonzero().squeeze(1)
+    assert torch.equal(bits16(a.act_buf[real]), bits16(b.act_buf[real]))
+    assert torch.equal(a.y_perm[real].view(torch.int32), b.y_perm[real].view(torch.int32))
+    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", list(W.CONFIGS))
