@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--workload", default="mixtral", choices=list(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle sample budget in seconds (0 disables the CPU baseline)")
+    ap.add_argument("--cu-partition", action="store_true",
+                    help="only run the CU-partition sweep (a copy of the remote-labelled token rows on nc CUs "
+                         "while the grouped FFN runs on the others) and print its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE against a known size) and exit")
@@ -107,6 +110,97 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": 4 * n, "copies": 5}), flush=True)
+
+
+def cu_partition(args):
+    """Stand-in for the communication/computation CU split of thread-block specialisation.
+
+    For nc in a sweep of whole XCDs (32-CU steps), two streams with
+    complementary CU masks (default priority) are created: a copy of the
+    token rows that come from other source ranks -- the bytes a dispatch
+    all-to-all would deliver -- runs on the CUs [0, nc) while the grouped FFN
+    runs on [nc, n); the library sizes its persistent grid to the stream's CU
+    mask.  Partitions that split an XCD leave that XCD with fewer CUs than
+    its round-robin share of a one-workgroup-per-CU grid, which then runs in
+    two waves (measured: 1.6-1.8x slower FFN at 8, 16 and 48 CUs), so the
+    sweep moves whole XCDs.  Reported per nc: the
+    FFN alone on its CUs, the FFN and the copy run together, the copy's rate,
+    and the FFN's slowdown against all CUs without the copy.
+    """
+    import ctypes
+    import torch
+    from mixture_experts_layer_moe_amd import workloads as W
+    from mixture_experts_layer_moe_amd.layer import MoELayer
+
+    name = args.workload if args.workload != "mixtral" else "ep_share"
+    cfg = W.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    d = W.make_inputs(cfg, dev)
+    layer = MoELayer.from_inputs(cfg, d)
+    layer.run()
+    torch.cuda.synchronize()
+    n = torch.cuda.get_device_properties(dev).multi_processor_count
+    src = d["src_rank"] if d["src_rank"] is not None else torch.ones(cfg.T, dtype=torch.int32, device=dev)
+    remote = ((src != 0) & (layer.perm.inv_perm >= 0).any(dim=1)).nonzero().squeeze(1)
+    rows = d["x"].index_select(0, remote)
+    staging = torch.empty_like(rows)
+    comm_bytes = 2 * rows.numel() * rows.element_size()
+    hip = ctypes.CDLL("libamdhip64.so")
+    words = (n + 31) // 32
+
+    def masked_stream(cus):
+        mask = (ctypes.c_uint32 * words)()
+        for c in cus:
+            mask[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask)
+        if err != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({err})")
+        return h, torch.cuda.ExternalStream(h.value, device=dev)
+
+    def timed(stream_f, stream_c, reps, with_comm):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ffn_ms, comm_ms, step_ms = [], [], []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e[0].record(stream_f)
+            stream_c.wait_event(e[0])
+            layer.ffn(stream_f)
+            e[1].record(stream_f)
+            if with_comm:
+                with torch.cuda.stream(stream_c):
+                    staging.copy_(rows)
+                e[2].record(stream_c)
+                stream_f.wait_event(e[2])
+            e[3].record(stream_f)
+            torch.cuda.synchronize()
+            ffn_ms.append(e[0].elapsed_time(e[1]))
+            if with_comm:
+                comm_ms.append(e[0].elapsed_time(e[2]))
+            step_ms.append(e[0].elapsed_time(e[3]))
+        med = lambda v: sorted(v)[len(v) // 2] if v else None
+        return med(ffn_ms), med(comm_ms), med(step_ms)
+
+    reps = max(3, min(args.steps, 20))
+    base = torch.cuda.current_stream()
+    full_ffn, _, _ = timed(base, base, reps, False)
+    curve = []
+    per_xcd = n // 8
+    for nc in (per_xcd, 2 * per_xcd, 3 * per_xcd, 4 * per_xcd):
+        if nc >= n:
+            break
+        hc, sc = masked_stream(range(nc))
+        hf, sf = masked_stream(range(nc, n))
+        alone, _, _ = timed(sf, sc, reps, False)
+        ffn, comm, step = timed(sf, sc, reps, True)
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(hc)
+        hip.hipStreamDestroy(hf)
+        curve.append({"comm_cus": nc, "ffn_alone_ms": round(alone, 4), "ffn_with_comm_ms": round(ffn, 4),
+                      "comm_ms": round(comm, 4), "comm_GBps": round(comm_bytes / (comm * 1e-3) / 1e9, 1),
+                      "step_ms": round(step, 4), "ffn_slowdown": round(ffn / full_ffn, 4)})
+    print(json.dumps({"cu_partition": name, "cus": n, "comm_rows": int(remote.numel()),
+                      "comm_bytes": comm_bytes, "ffn_all_cus_ms": round(full_ffn, 4), "curve": curve}), flush=True)
 
 
 def cpu_baseline(cfg, d, seconds):
@@ -207,6 +301,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cu_partition:
+        cu_partition(args)
         return
 
     import torch

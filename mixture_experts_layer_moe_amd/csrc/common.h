@@ -55,6 +55,7 @@ struct FfnArgs {
   const int32_t* row_src;
   int topk;
   int64_t T;
+  int cus;  // CUs the launch stream may use (set by launch_grouped_ffn)
   hipStream_t stream;
 };
 size_t grouped_ffn_ws_bytes(int tile_m, int H);

@@ -698,10 +698,22 @@ int num_cus() {
   return cached[dev];
 }
 
-// Persistent grid: one workgroup per CU (a multiple of the XCD count), fewer if there are fewer items.
-int64_t persistent_grid(int64_t max_items) {
-  int64_t grid = num_cus();
-  grid = (grid + kXcds - 1) / kXcds * kXcds;
+// CUs that kernels launched on stream s may use: the popcount of its CU mask
+// (a stream created with hipExtStreamCreateWithCUMask), else every CU.
+int stream_cus(hipStream_t s) {
+  const int n = num_cus();
+  uint32_t mask[32] = {0};  // up to 1024 CUs
+  if (n > 1024 || hipExtStreamGetCUMask(s, 32, mask) != hipSuccess) return n;
+  int c = 0;
+  for (uint32_t m : mask) c += __builtin_popcount(m);
+  return (c > 0 && c < n) ? c : n;
+}
+
+// Persistent grid: one workgroup per usable CU, rounded down to a multiple of
+// the XCD count (so every workgroup is resident at once), fewer if there are
+// fewer items.
+int64_t persistent_grid(int64_t max_items, int cus) {
+  int64_t grid = cus >= kXcds ? cus / kXcds * kXcds : kXcds;
   if (max_items < grid) grid = (max_items + kXcds - 1) / kXcds * kXcds;
   if (grid < kXcds) grid = kXcds;
   return grid;
@@ -710,7 +722,7 @@ int64_t persistent_grid(int64_t max_items) {
 template <typename Kern, typename... Extra>
 hipError_t launch_persistent(Kern kern, int threads, int64_t max_items, const uint16_t* A, const uint16_t* B0,
                              const uint16_t* B1, int N, int K, const FfnArgs& a, void* C, Extra... extra) {
-  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items)), dim3(threads), 0, a.stream, A, B0, B1, N, K,
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(max_items, a.cus)), dim3(threads), 0, a.stream, A, B0, B1, N, K,
                      a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, C, extra...);
   return hipGetLastError();
 }
@@ -725,7 +737,7 @@ hipError_t launch_layer1(const FfnArgs& a) {
   hipError_t e = launch_persistent(gemm_mfma32_kernel<BM, BN, false, EPI_F32, ORDER_N, ST, true, false>, 256, max_items,
                                    a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, static_cast<float*>(a.ws), (const int32_t*)nullptr, 0, (int64_t)0);
   if (e != hipSuccess) return e;
-  const int G = (int)persistent_grid(max_items);
+  const int G = (int)persistent_grid(max_items, a.cus);
   hipLaunchKernelGGL((reduce_slices_kernel<BM, BN, ORDER_N>), dim3((unsigned)(G * (BM / 16))), dim3(256), 0, a.stream,
                      static_cast<const float*>(a.ws), a.H, a.F, G, a.counts, a.offsets, a.tiles, a.num_tiles,
                      a.tiles_cap, a.R_cap, a.E_loc, a.y_perm);
@@ -780,10 +792,12 @@ size_t grouped_ffn_ws_bytes(int tile_m, int H) {
   // Split-K partial tiles of layer1's last round: at most one round of items.
   if (tile_m < 128) return 0;
   const int bn = H % 256 == 0 ? 256 : 128;
-  return (size_t)persistent_grid(INT32_MAX) * tile_m * bn * sizeof(float);
+  return (size_t)persistent_grid(INT32_MAX, num_cus()) * tile_m * bn * sizeof(float);
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs& a) {
+hipError_t launch_grouped_ffn(const FfnArgs& args) {
+  FfnArgs a = args;
+  a.cus = stream_cus(a.stream);  // the same grid for every launch of this call
   switch (a.tile_m) {
     case 256: return launch_big<256, 128, 2, 256, 2>(a);
     case 128: return launch_big<128, 128, 3, 256, 3>(a);
