@@ -18,8 +18,6 @@ __device__ __forceinline__ uint16_t f2bf_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 // ---------------------------------------------------------------------------
 // Internal launchers (implemented in the .hip files; called by moe_api.hip
 // after argument validation).  All return hipGetLastError() after launching.

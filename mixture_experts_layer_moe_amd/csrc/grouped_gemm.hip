@@ -10,15 +10,17 @@
 //     independent), layer1 along N (the top-k reduce couples rows across
 //     experts);
 //   - section 4: the MoE GEMMs avoid re-reading row indices from global
-//     memory on every K iteration (here the rows are already contiguous, so
-//     a tile needs only its first row and its expert).
+//     memory on every K iteration: with the permuted copy a tile needs only
+//     its first row and its expert; the gathered layer0 (GATHER) reads each
+//     lane's token-row offsets once per work item and keeps them in
+//     registers for the whole K loop.
 // Tile-level-signalling follow-up (abstract): a persistent kernel covers all
 // local experts without relaunches.
 //
 // Design (MI355X / CDNA4):
-//   * Persistent grid of one workgroup per CU; the work items are (row tile,
-//     column block) pairs read from the device tile list, so the host never
-//     needs the per-expert row counts.
+//   * Persistent grid of one workgroup per CU the launch stream may use (its
+//     CU mask); the work items are (row tile, column block) pairs read from
+//     the device tile list, so the host never needs the per-expert row counts.
 //   * Workgroup ids are remapped so that each XCD (workgroups are dispatched
 //     round-robin over the 8 XCDs) runs a contiguous run of work items: the
 //     items an XCD runs together form a small rectangle of row tiles x
@@ -27,9 +29,10 @@
 //     inside a group, column block major then tile.  Layer1 order: column
 //     groups of kGroupN blocks (N-decomposition: a column group is finished
 //     for all tiles before the next starts); inside a group, tile major.
-//   * Operands are staged HBM -> LDS with global_load_lds_dwordx4 (16 bytes
-//     per lane straight into LDS, no VGPR round trip) in a ring of STAGES
-//     buffers, BK = 64.  Each LDS row holds 64 bf16 (128 B) of one operand
+//   * Operands are staged HBM -> LDS with direct-to-LDS loads (16 bytes per
+//     lane straight into LDS, no VGPR round trip: buffer_load_dwordx4 ... lds
+//     for big tiles, global_load_lds_dwordx4 for small ones) in a ring of
+//     STAGES buffers, BK = 64.  Each LDS row holds 64 bf16 (128 B) of one operand
 //     row; the 16-byte chunk index is XOR-swizzled with
 //     (row & 7) ^ ((row >> 3) & 1), so that the fragment reads (consecutive
 //     lanes read consecutive rows at one chunk) hit distinct banks both for
@@ -57,6 +60,9 @@
 //   * Epilogue: SwiGLU silu(g) * u, or exact-erf GELU, in fp32, rounded to
 //     bf16 (nearest even) for layer0; plain fp32 for layer1.  Rows past the
 //     expert's real count are never stored.
+//   * Last scheduling round: the items left after the whole rounds run as
+//     half-width pieces, or (layer1 with a workspace) as K slices summed in
+//     order by reduce_slices_kernel.
 #include "common.h"
 
 namespace moe {
@@ -95,24 +101,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Load ROWS operand rows x 64 bf16 (row stride ld elements) into a swizzled
-// LDS tile with direct-to-LDS loads: one wave instruction moves 8 rows; lane
-// L writes physical chunk L % 8 of row L / 8 and fetches the logical chunk
-// that belongs there.
-template <int ROWS, int NWAVES>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ g, int64_t ld, char* lds,
-                                           int wave, int lane) {
-  static_assert(ROWS % (8 * NWAVES) == 0, "rows per wave");
-  const int r_in = lane >> 3;                  // row within the 8-row group
-#pragma unroll
-  for (int q = 0; q < ROWS / (8 * NWAVES); ++q) {
-    const int grp = q * NWAVES + wave;
-    const int chunk = (lane & 7) ^ swz(grp * 8 + r_in);
-    const uint16_t* src = g + (int64_t)(grp * 8 + r_in) * ld + chunk * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + grp * 1024), 16, 0, 0);
-  }
-}
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* tile, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz(row)) << 4));
