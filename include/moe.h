@@ -161,7 +161,8 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
  * round of layer1 splits its tiles along K into fp32 partials that a second
  * kernel sums in a fixed order, so the result stays deterministic.  A
  * non-NULL ws that is too small returns MOE_ERR_WORKSPACE.
- * Requires H % 128 == 0, F % 128 == 0, tile_m in {16, 32, 64, 128, 256}.
+ * Requires H % 128 == 0, F % 128 == 0, H <= 1048576, F <= 1048576,
+ * tile_m in {16, 32, 64, 128, 256}.
  */
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
                            const int32_t* expert_offsets, const int32_t* tiles,

@@ -217,8 +217,8 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   const int64_t b_expert = (int64_t)N * K;
 
   // Buffer resources based at this item's operand panels (ranges of a few MiB,
-  // out-of-range reads return zeros).  A and B share the row stride K, so one
-  // per-lane byte offset serves every direct-to-LDS load of this wave:
+  // out-of-range reads return zeros).  The weight panels share the row stride
+  // K, so one per-lane byte offset serves every weight load of this wave:
   // row (q * NWAVES + wave) * 8 + lane / 8, logical chunk swizzled for that row.
   const __amdgpu_buffer_rsrc_t ra = GATHER ? make_rsrc(A, T * K * 2) : make_rsrc(A + (int64_t)row0 * K, BM * K * 2);
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + le * b_expert + (int64_t)n0 * K, BN * K * 2);
@@ -226,15 +226,21 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   const __amdgpu_buffer_rsrc_t rnone = make_rsrc(A, 0);  // no records: every load reads zero, fetches nothing
   const int r_in = lane >> 3;
   const uint32_t voff = (uint32_t)(((wave * 8 + r_in) * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2);
-  // GATHER: per A load, this lane's byte offset into x (its token row, same
-  // swizzled chunk); out of range for padding rows, which then read zeros.
-  uint32_t voff_a[GATHER ? A_PIECES : 1];
-  if (GATHER) {
+  // Per A load q, this lane's byte offset: its row of the token panel (GATHER:
+  // its token's row of x), same swizzled chunk.  Rows past the expert's real
+  // count (GATHER: padding rows) get an offset past every resource, so they
+  // read zeros and fetch nothing, and their MFMAs multiply zeros.
+  const uint32_t chunk_b = (uint32_t)((((lane & 7) ^ r_in ^ (wave & 1)) * 8) * 2);
+  uint32_t voff_a[A_PIECES];
 #pragma unroll
-    for (int q = 0; q < A_PIECES; ++q) {
-      const int src = row_src[row0 + (q * NWAVES + wave) * 8 + r_in];
+  for (int q = 0; q < A_PIECES; ++q) {
+    const int r = (q * NWAVES + wave) * 8 + r_in;
+    if (GATHER) {
+      const int src = row_src[row0 + r];
       const int64_t t = src >= 0 ? src / topk : -1;
-      voff_a[q] = (t >= 0 && t < T) ? (uint32_t)((t * K + (((lane & 7) ^ r_in ^ (wave & 1)) * 8)) * 2) : 0x80000000u;
+      voff_a[q] = (t >= 0 && t < T) ? (uint32_t)(t * K * 2) + chunk_b : 0x80000000u;
+    } else {
+      voff_a[q] = r < valid ? (uint32_t)(r * K * 2) + chunk_b : 0x80000000u;
     }
   }
   floatx16 acc[NMAT][TN][TM];
@@ -255,12 +261,11 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
     const bool is_a = p < A_PIECES;
     const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
     const int lds_off = (is_a ? 0 : A_BYTES + m * BN * 128) + (q * NWAVES + wave) * 1024;
-    const bool g = GATHER && is_a;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? a : (m ? b1 : b0), (lds_void*)(smem + stage * STAGE + lds_off), 16,
-                                             vo, ((g ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0, 0);
+                                             vo, ((is_a ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0, 0);
   };
-// Byte offset of this lane for load p: its gathered token row for an A load, else the shared one.
-#define MOE_VOFF(p) (GATHER && (p) < A_PIECES ? voff_a[GATHER && (p) < A_PIECES ? (p) : 0] : voff)
+// Byte offset of this lane for load p: its own row for an A load, else the shared weight-row one.
+#define MOE_VOFF(p) ((p) < A_PIECES ? voff_a[(p) < A_PIECES ? (p) : 0] : voff)
   struct Frags {
     bf16x8 a[TM];
     bf16x8 b[NMAT][TN];

@@ -121,6 +121,7 @@ moe_status grouped_ffn_impl(const void* x_perm, const void* x, const int32_t* ro
   if (act != MOE_ACT_GELU && act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
   if ((act == MOE_ACT_SWIGLU) != (w0_up != nullptr)) return MOE_ERR_INVALID_ARG;
   if (H % 128 != 0 || F % 128 != 0 || !tile_m_ok(tile_m)) return MOE_ERR_UNSUPPORTED;
+  if (H > (1 << 20) || F > (1 << 20)) return MOE_ERR_UNSUPPORTED;  // 32-bit operand-panel offsets
   if (R_cap > INT32_MAX || tiles_cap > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   const bool gather = x_perm == nullptr;
   if (gather) {

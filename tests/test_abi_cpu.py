@@ -122,6 +122,8 @@ def test_grouped_ffn_validation(L):
     assert ffn_call(L, act=7) == INVALID
     assert ffn_call(L, H=576) == UNSUPPORTED          # H % 128
     assert ffn_call(L, F=1000) == UNSUPPORTED
+    assert ffn_call(L, F=(1 << 20) + 128) == UNSUPPORTED   # operand panels need 32-bit offsets
+    assert ffn_call(L, H=(1 << 20) + 128) == UNSUPPORTED
     assert ffn_call(L, tm=8) == UNSUPPORTED
     assert ffn_call(L, y=NULL) == INVALID
     assert ffn_call(L, Rcap=0) == OK                  # no rows: nothing launched
