@@ -79,7 +79,7 @@ size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E_loc, int32_t 
 /* Bytes of optional device workspace for moe_grouped_ffn with this tile_m and
  * H on the current device (0 for tile_m <= 64, which never uses it; 0 on
  * invalid arguments).  The workspace holds fp32 partial tiles: one CU-count's
- * worth of tile_m x 256 (or x 128) blocks. */
+ * worth of tile_m x 256 blocks. */
 size_t moe_grouped_ffn_workspace_bytes(int32_t tile_m, int32_t H);
 
 /*
@@ -158,9 +158,11 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
  * capacities they were allocated with.  Accumulation is fp32.
  * ws / ws_bytes: optional device scratch (NULL / 0 is allowed) of at least
  * moe_grouped_ffn_workspace_bytes(tile_m, H); with it, the last scheduling
- * round of layer1 splits its tiles along K into fp32 partials that a second
- * kernel sums in a fixed order, so the result stays deterministic.  A
- * non-NULL ws that is too small returns MOE_ERR_WORKSPACE.
+ * round of each layer splits its tiles along K into fp32 partials that a
+ * second kernel sums in a fixed order (and then applies layer0's
+ * activation), so the result stays deterministic; it can differ from the
+ * result without ws by fp32 summation order (layer0: by an ulp of the bf16
+ * activation).  A non-NULL ws that is too small returns MOE_ERR_WORKSPACE.
  * Requires H % 128 == 0, F % 128 == 0, H <= 1048576, F <= 1048576,
  * tile_m in {16, 32, 64, 128, 256}.
  */

@@ -61,8 +61,11 @@
 //     bf16 (nearest even) for layer0; plain fp32 for layer1.  Rows past the
 //     expert's real count are never stored.
 //   * Last scheduling round: the items left after the whole rounds run as
-//     half-width pieces, or (layer1 with a workspace) as K slices summed in
-//     order by reduce_slices_kernel.
+//     half-width pieces, or (with a workspace) as up to 8 K slices whose fp32
+//     partials reduce_slices_kernel sums in order before the layer's
+//     epilogue (layer0's activation included).
+//   * Token rows past an expert's real count read as zeros (out-of-range
+//     buffer offsets): they fetch nothing and their MFMAs multiply zeros.
 #include "common.h"
 
 namespace moe {
@@ -74,7 +77,8 @@ constexpr int kGroupN = 4;      // layer1: column blocks per column group
 constexpr int kXcds = 8;
 constexpr int MOE_ACT_SWIGLU_I = 1;  // moe_act value of SwiGLU
 
-enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_F32 = 2 };
+// EPI_PARTIAL: raw fp32 partial sums of a K slice, the up matrix's (DUAL) in the columns after the gate's.
+enum Epi { EPI_GELU = 0, EPI_SWIGLU = 1, EPI_F32 = 2, EPI_PARTIAL = 3 };
 enum Order { ORDER_M = 0, ORDER_N = 1 };
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
@@ -163,6 +167,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) { return (bid % kXcds) 
 // Epilogue for 4 consecutive output columns of one row.
 template <int EPI>
 __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const float* g, const float* u) {
+  static_assert(EPI != EPI_PARTIAL, "partial tiles are stored as two fp32 halves");
   if (EPI == EPI_F32) {
     *reinterpret_cast<floatx4*>(static_cast<float*>(C) + row * N + n) = floatx4{g[0], g[1], g[2], g[3]};
   } else {
@@ -410,7 +415,12 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
           g[r] = acc[0][j][i][q * 4 + r];
           u[r] = acc[NMAT - 1][j][i][q * 4 + r];
         }
-        store4<EPI>(C, row, ldc, n, g, u);
+        if constexpr (EPI == EPI_PARTIAL) {
+          store4<EPI_F32>(C, row, ldc, n, g, g);
+          if (NMAT == 2) store4<EPI_F32>(C, row, ldc, n + BN, u, u);
+        } else {
+          store4<EPI>(C, row, ldc, n, g, u);
+        }
       }
   }
   wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
@@ -424,22 +434,25 @@ constexpr int big_lds_bytes(int stages) {
 
 // Number of K slices of each last-round item (1 = no split) when the rem
 // items left after the whole rounds are split along K: as many slices as fit
-// in one round of G workgroups, at most 4, dividing the nk stages of K.
+// in one round of G workgroups, at most kMaxSlices and at most the nk stages
+// of K.  Slice s covers stages [s * nk / S, (s + 1) * nk / S).
+constexpr int kMaxSlices = 8;
 __host__ __device__ inline int tail_ksplit(int64_t rem, int G, int nk) {
   if (rem <= 0) return 1;
-  int S = (int)(G / rem);
-  S = S > 4 ? 4 : S;
-  while (S > 1 && nk % S != 0) --S;
-  return S < 1 ? 1 : S;
+  int64_t S = G / rem;
+  S = S > kMaxSlices ? kMaxSlices : S;
+  S = S > nk ? nk : S;
+  return S < 1 ? 1 : (int)S;
 }
 
 // Persistent kernel over (row tile, column block) items.  With G workgroups
 // and W items, the first floor(W / G) * G items run whole (every workgroup
 // gets the same number).  The remaining items run in one more round:
-//  * with SPLITK (layer1 only: its epilogue is linear) and S = tail_ksplit
-//    > 1, each is split into S slices of K whose fp32 partial tiles go to ws
-//    (piece p at ws + p * BM * BN, row-major BM x BN); reduce_slices_kernel
-//    sums them in slice order afterwards, so the result is deterministic;
+//  * with SPLITK and S = tail_ksplit > 1, each is split into S slices of K
+//    whose fp32 partial tiles go to ws (piece p at ws + p * BM * NMAT * BN,
+//    row-major, the up matrix's columns after the gate's);
+//    reduce_slices_kernel sums them in slice order afterwards (and applies
+//    layer0's activation), so the result is deterministic;
 //  * otherwise each is split into two half-width pieces.
 // Either way the last round costs a fraction of a full item instead of
 // leaving most CUs idle behind a few full ones.
@@ -452,7 +465,6 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
     int64_t R_cap, int E_loc, void* __restrict__ C, float* __restrict__ ws, const int32_t* __restrict__ row_src,
     int topk, int64_t T) {
-  static_assert(!SPLITK || EPI == EPI_F32, "K slices need a linear epilogue");
   __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN, DUAL>(STAGES)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
@@ -484,13 +496,15 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
                                                  wave, lane, row_src, topk, T);
   }
   if (S > 1) {
-    const int k_len = K / S;
+    constexpr int PIECE = BM * (DUAL ? 2 : 1) * BN;  // floats per partial tile
+    const int nk = K / BK;
     for (int64_t piece = vid; piece < S * (total - full); piece += G) {
       int le, row0, valid, n0;
       if (!coords(full + piece / S, le, row0, valid, n0)) continue;
-      gemm_item<BM, BN, DUAL, EPI, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0,
-                                                   (int)(piece % S) * k_len, k_len, ws + piece * (int64_t)(BM * BN), 0,
-                                                   BN, 0, wave, lane, row_src, topk, T);
+      const int s = (int)(piece % S), kb = s * nk / S, ke = (s + 1) * nk / S;
+      gemm_item<BM, BN, DUAL, EPI_PARTIAL, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0, kb * BK,
+                                                           (ke - kb) * BK, ws + piece * (int64_t)PIECE, 0,
+                                                           (DUAL ? 2 : 1) * BN, 0, wave, lane, row_src, topk, T);
     }
     return;
   }
@@ -504,16 +518,19 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
 }
 
 // Sums the K slices that gemm_mfma32_kernel<..., SPLITK> left in ws for its
-// last-round items (same G, tile list and shapes) into C's valid rows, slice
-// by slice in order.  Block b covers rows [(b % (BM / RB)) * RB, + RB) of unit
-// b / (BM / RB); launched with G * BM / RB blocks of 256 threads.
-template <int BM, int BN, int ORDER>
+// last-round items (same G, tile list and shapes), slice by slice in order,
+// and stores the valid rows through the layer's epilogue EPI (fp32 for
+// layer1; the activation, rounded to bf16, for layer0, whose DUAL partial
+// tiles hold the up matrix's columns after the gate's).  Block b covers rows
+// [(b % (BM / RB)) * RB, + RB) of unit b / (BM / RB); launched with
+// G * BM / RB blocks of 256 threads.
+template <int BM, int BN, bool DUAL, int EPI, int ORDER>
 __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restrict__ ws, int N, int K, int G,
                                                             const int32_t* __restrict__ counts,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ tiles,
                                                             const int32_t* __restrict__ num_tiles, int64_t tiles_cap,
-                                                            int64_t R_cap, int E_loc, float* __restrict__ C) {
+                                                            int64_t R_cap, int E_loc, void* __restrict__ C) {
   constexpr int RB = 16;
   int nt = *num_tiles;
   if (nt > tiles_cap) nt = (int)tiles_cap;
@@ -529,14 +546,19 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
   if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) return;
   int valid = counts[le] - (row0 - offsets[le]);
   valid = valid < BM ? valid : BM;
-  const floatx4* part = reinterpret_cast<const floatx4*>(ws + u * S * (int64_t)(BM * BN));
+  constexpr int NMAT = DUAL ? 2 : 1, W4 = NMAT * BN / 4;  // float4 groups per partial row
+  const floatx4* part = reinterpret_cast<const floatx4*>(ws + u * S * (int64_t)(BM * NMAT * BN));
   for (int e = threadIdx.x; e < RB * (BN / 4); e += 256) {
     const int m = rc * RB + e / (BN / 4), c4 = e % (BN / 4);
     if (m >= valid) continue;
-    const int idx = m * (BN / 4) + c4;
-    floatx4 acc = part[idx];
-    for (int q = 1; q < S; ++q) acc += part[q * (BM * BN / 4) + idx];
-    *reinterpret_cast<floatx4*>(C + (int64_t)(row0 + m) * N + nb * BN + c4 * 4) = acc;
+    const int idx = m * W4 + c4;
+    floatx4 g4 = part[idx], u4 = part[idx + (NMAT - 1) * (BN / 4)];
+    for (int q = 1; q < S; ++q) {
+      g4 += part[q * (BM * W4) + idx];
+      if (DUAL) u4 += part[q * (BM * W4) + idx + BN / 4];
+    }
+    const float g[4] = {g4[0], g4[1], g4[2], g4[3]}, uu[4] = {u4[0], u4[1], u4[2], u4[3]};
+    store4<EPI>(C, (int64_t)row0 + m, N, nb * BN + c4 * 4, g, uu);
   }
 }
 
@@ -731,24 +753,38 @@ hipError_t launch_layer1(const FfnArgs& a) {
                                    a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, static_cast<float*>(a.ws), (const int32_t*)nullptr, 0, (int64_t)0);
   if (e != hipSuccess) return e;
   const int G = (int)persistent_grid(max_items, a.cus);
-  hipLaunchKernelGGL((reduce_slices_kernel<BM, BN, ORDER_N>), dim3((unsigned)(G * (BM / 16))), dim3(256), 0, a.stream,
-                     static_cast<const float*>(a.ws), a.H, a.F, G, a.counts, a.offsets, a.tiles, a.num_tiles,
-                     a.tiles_cap, a.R_cap, a.E_loc, a.y_perm);
+  hipLaunchKernelGGL((reduce_slices_kernel<BM, BN, false, EPI_F32, ORDER_N>), dim3((unsigned)(G * (BM / 16))), dim3(256),
+                     0, a.stream, static_cast<const float*>(a.ws), a.H, a.F, G, a.counts, a.offsets, a.tiles,
+                     a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, a.y_perm);
   return hipGetLastError();
 }
 
 // tile_m >= 128: layer0 = BM x (BN0 gate + BN0 up) (GELU: BM x BN0), layer1 = BM x BN1
 // (BM x 128 when H is not a multiple of BN1).
-// Layer0 over BM x BN0 items, reading the token rows from x_perm or (GATHER) from x.
-template <int BM, int BN0, int ST0, bool GATHER>
-hipError_t launch_big_layer0(const FfnArgs& a) {
+// Layer0 over BM x BN0 items (DUAL: gate and up), reading the token rows from
+// x_perm or (GATHER) from x; with a workspace the last round is split along K.
+template <int BM, int BN0, int ST0, bool DUAL, int EPI, bool GATHER>
+hipError_t launch_layer0(const FfnArgs& a) {
   const int64_t items = a.tiles_cap * (a.F / BN0);
   const uint16_t* A = GATHER ? a.x : a.x_perm;
-  if (a.act == MOE_ACT_SWIGLU_I)
-    return launch_persistent(gemm_mfma32_kernel<BM, BN0, true, EPI_SWIGLU, ORDER_M, ST0, false, GATHER>, 256, items, A,
-                             a.w0, a.w0_up, a.F, a.H, a, a.act_buf, (float*)nullptr, a.row_src, a.topk, a.T);
-  return launch_persistent(gemm_mfma32_kernel<BM, BN0, false, EPI_GELU, ORDER_M, ST0, false, GATHER>, 256, items, A,
-                           a.w0, nullptr, a.F, a.H, a, a.act_buf, (float*)nullptr, a.row_src, a.topk, a.T);
+  const uint16_t* B1 = DUAL ? a.w0_up : nullptr;
+  if (a.ws == nullptr)
+    return launch_persistent(gemm_mfma32_kernel<BM, BN0, DUAL, EPI, ORDER_M, ST0, false, GATHER>, 256, items, A, a.w0,
+                             B1, a.F, a.H, a, a.act_buf, (float*)nullptr, a.row_src, a.topk, a.T);
+  hipError_t e = launch_persistent(gemm_mfma32_kernel<BM, BN0, DUAL, EPI, ORDER_M, ST0, true, GATHER>, 256, items, A,
+                                   a.w0, B1, a.F, a.H, a, a.act_buf, static_cast<float*>(a.ws), a.row_src, a.topk, a.T);
+  if (e != hipSuccess) return e;
+  const int G = (int)persistent_grid(items, a.cus);
+  hipLaunchKernelGGL((reduce_slices_kernel<BM, BN0, DUAL, EPI, ORDER_M>), dim3((unsigned)(G * (BM / 16))), dim3(256),
+                     0, a.stream, static_cast<const float*>(a.ws), a.F, a.H, G, a.counts, a.offsets, a.tiles,
+                     a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc, a.act_buf);
+  return hipGetLastError();
+}
+
+template <int BM, int BN0, int ST0, bool GATHER>
+hipError_t launch_big_layer0(const FfnArgs& a) {
+  if (a.act == MOE_ACT_SWIGLU_I) return launch_layer0<BM, BN0, ST0, true, EPI_SWIGLU, GATHER>(a);
+  return launch_layer0<BM, BN0, ST0, false, EPI_GELU, GATHER>(a);
 }
 
 template <int BM, int BN0, int ST0, int BN1, int ST1>
@@ -782,10 +818,11 @@ hipError_t launch_small(const FfnArgs& a) {
 }  // namespace
 
 size_t grouped_ffn_ws_bytes(int tile_m, int H) {
-  // Split-K partial tiles of layer1's last round: at most one round of items.
+  // Split-K partial tiles of either layer's last round: at most one round of
+  // pieces of tile_m x 256 fp32 (layer1's BM x 256, layer0's BM x (128 gate + 128 up)).
+  (void)H;
   if (tile_m < 128) return 0;
-  const int bn = H % 256 == 0 ? 256 : 128;
-  return (size_t)persistent_grid(INT32_MAX, num_cus()) * tile_m * bn * sizeof(float);
+  return (size_t)persistent_grid(INT32_MAX, num_cus()) * tile_m * 256 * sizeof(float);
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& args) {
