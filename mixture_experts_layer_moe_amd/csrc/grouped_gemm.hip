@@ -83,6 +83,7 @@ enum Order { ORDER_M = 0, ORDER_N = 1 };
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;  // one 16-byte load
 
 // silu(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each, far below the
 // bf16 rounding that follows).
@@ -318,27 +319,10 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int SPREAD = (2 * LOADS + NMFMA - 1) / NMFMA < BK / 16 - 1 ? (2 * LOADS + NMFMA - 1) / NMFMA : BK / 16 - 1;
   constexpr int PER_STEP = (LOADS + SPREAD - 1) / SPREAD;
 
-  // Ring schedule: the prologue loads stages 0 .. STAGES-2; iteration kt
-  // (computing stage kt) loads stage kt + STAGES - 1 into buffer
-  // (kt - 1) mod STAGES, which every wave has finished reading at the barrier
-  // that ended iteration kt - 1 (and which the prologue left empty for
-  // kt = 0).  A stage past the end is "loaded" through resources with no
-  // records: every lane reads zero, nothing is fetched, and the zeros land in
-  // that free buffer, so the schedule is the same in every iteration.
-#pragma unroll
-  for (int st = 0; st + 1 < STAGES; ++st)
-    if (st < nk)
-#pragma unroll
-      for (int p = 0; p < LOADS; ++p) load(p, st, st * BK, ra, rb0, rb1, MOE_VOFF(p));
-  {  // stage 0 has landed once only the prologue's later stages are in flight
-    const int later = (nk < STAGES - 1 ? nk : STAGES - 1) - 1;
-    wait_stages<LOADS, STAGES - 2>(later);
-  }
-  ring_barrier();
-  Frags cur = read_frags(0, 0);
-  // K steps of one stage but the last: the next step's fragments are read
-  // while this step's MFMAs issue; with LD, steps below SPREAD also issue
-  // their share of the loads of stage TS into buffer TBUF through (RA, RB0, RB1).
+// K steps of one stage but the last: the next step's fragments are read
+// while this step's MFMAs issue; with LD, steps below SPREAD also issue
+// their share of the direct-to-LDS loads of stage TS into buffer TBUF
+// through (RA, RB0, RB1).
 #define MOE_INNER_STEPS(BUF, LD, TBUF, TS, RA, RB0, RB1)                              \
   _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {                        \
   const int np_ = (LD) && ks < SPREAD                                               \
@@ -367,6 +351,107 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   __builtin_amdgcn_sched_barrier(0);                                                \
   cur = nxt;                                                                        \
   }
+  Frags cur;
+  if constexpr (STAGES == 2) {
+  // Two LDS buffers and one register stage: iteration kt computes stage kt
+  // from buffer kt % 2 while it writes stage kt+1, which arrived in
+  // registers during iteration kt-1, into the other buffer and loads stage
+  // kt+2 into those registers.  A load has a whole K stage to land, its
+  // LDS write is spread over the MFMAs, and the plain vector loads move
+  // more bytes per CU than direct-to-LDS ones when the tile streams from
+  // L2.  Load p of a stage goes to the same LDS place as the direct-to-LDS
+  // load p would, so the fragment reads are shared with the ring below.
+  u32x4 stg[LOADS];
+  auto vload = [&](int p, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0, __amdgpu_buffer_rsrc_t b1,
+                   uint32_t vo) {
+    const bool is_a = p < A_PIECES;
+    const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
+    stg[p] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? a : (m ? b1 : b0), vo,
+                                                   ((is_a ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0);
+  };
+  auto vwrite = [&](int p, int buf) {
+    const bool is_a = p < A_PIECES;
+    const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
+    const int lds_off = (is_a ? 0 : A_BYTES + m * BN * 128) + (q * NWAVES + wave) * 1024;
+    *reinterpret_cast<u32x4*>(smem + buf * STAGE + lds_off + lane * 16) = stg[p];
+  };
+  // Prologue: stage 0 into buffer 0, stage 1 into the registers.
+#pragma unroll
+  for (int p = 0; p < LOADS; ++p) vload(p, 0, ra, rb0, rb1, MOE_VOFF(p));
+#pragma unroll
+  for (int p = 0; p < LOADS; ++p) vwrite(p, 0);
+#pragma unroll
+  for (int p = 0; p < LOADS; ++p)
+    vload(p, BK, 1 < nk ? ra : rnone, 1 < nk ? rb0 : rnone, 1 < nk ? rb1 : rnone, MOE_VOFF(p));
+  wait_lgkm0();
+  ring_barrier();
+  cur = read_frags(0, 0);
+// K steps of one stage but the last: the next step's fragments are read
+// from BUF while this step's MFMAs issue; steps below SPREAD also write their
+// share of the registers into WBUF and reload them from K offset KN through
+// (RA, RB0, RB1), each write before the load that reuses its registers.
+#define MOE_INNER_STEPS_VL(BUF, WBUF, KN, RA, RB0, RB1)                               \
+  _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {                        \
+  const int np_ = ks < SPREAD ? (LOADS - ks * PER_STEP < PER_STEP ? LOADS - ks * PER_STEP : PER_STEP) : 0; \
+  Frags nxt;                                                                        \
+  _Pragma("unroll") for (int t = 0; t < NREAD; ++t) read_one(nxt, (BUF), ks + 1, t); \
+  _Pragma("unroll") for (int t = 0; t < np_; ++t) {                                 \
+    vwrite(ks * PER_STEP + t, (WBUF));                                              \
+    vload(ks * PER_STEP + t, (KN), (RA), (RB0), (RB1), MOE_VOFF(ks * PER_STEP + t)); \
+  }                                                                                 \
+  MOE_MFMAS(cur, 0, NMFMA)                                                          \
+  if (np_ > 0)                                                                      \
+  _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                  \
+  _Pragma("unroll") for (int j = 0; j < TN; ++j)                                    \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i) asm volatile("" : "+a"(acc[m][j][i])); \
+  _Pragma("unroll") for (int t = 0; t < NMFMA + NREAD + 2 * LOADS; ++t) {          \
+    if (t < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               \
+    if (t < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               \
+    else if (t < NREAD + 2 * np_) {                                                 \
+      if ((t - NREAD) % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  \
+      else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                       \
+    }                                                                               \
+  }                                                                                 \
+  __builtin_amdgcn_sched_barrier(0);                                                \
+  cur = nxt;                                                                        \
+  }
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    // Buffer wbuf held stage kt-1, which every wave finished reading before
+    // the barrier that ended iteration kt-1.  A stage past the end is loaded
+    // through resources with no records (zeros, nothing fetched).
+    const int buf = kt & 1, wbuf = buf ^ 1;
+    const bool real = kt + 2 < nk;
+    MOE_INNER_STEPS_VL(buf, wbuf, (kt + 2) * BK, real ? ra : rnone, real ? rb0 : rnone, real ? rb1 : rnone)
+    MOE_MFMAS(cur, 0, NMFMA / 2)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();     // this wave's reads of stage kt and writes of stage kt+1 are complete
+    ring_barrier();   // stage kt+1 visible to all; buffer kt % 2 is free from the next iteration on
+    __builtin_amdgcn_sched_barrier(0);
+    const Frags nxt = read_frags(wbuf, 0);
+    MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+#undef MOE_INNER_STEPS_VL
+  } else {
+  // STAGES-deep ring of direct-to-LDS loads: the prologue loads stages 0 .. STAGES-2; iteration kt
+  // (computing stage kt) loads stage kt + STAGES - 1 into buffer
+  // (kt - 1) mod STAGES, which every wave has finished reading at the barrier
+  // that ended iteration kt - 1 (and which the prologue left empty for
+  // kt = 0).  A stage past the end is "loaded" through resources with no
+  // records: every lane reads zero, nothing is fetched, and the zeros land in
+  // that free buffer, so the schedule is the same in every iteration.
+#pragma unroll
+  for (int st = 0; st + 1 < STAGES; ++st)
+    if (st < nk)
+#pragma unroll
+      for (int p = 0; p < LOADS; ++p) load(p, st, st * BK, ra, rb0, rb1, MOE_VOFF(p));
+  {  // stage 0 has landed once only the prologue's later stages are in flight
+    const int later = (nk < STAGES - 1 ? nk : STAGES - 1) - 1;
+    wait_stages<LOADS, STAGES - 2>(later);
+  }
+  ring_barrier();
+  cur = read_frags(0, 0);
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int buf = kt % STAGES;
     const int ts = kt + STAGES - 1;
@@ -387,6 +472,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
     MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
+  }
   }
   {  // the last stage
     const int buf = (nk - 1) % STAGES;
