@@ -34,7 +34,6 @@ namespace {
 constexpr int kChunk = 256;         // tokens per chunk (one block of kernel A)
 constexpr int kScanThreads = 1024;  // block size of kernel B
 constexpr int kMaxExperts = 4096;   // E_loc * num_ranks <= 4096 (validated on the host)
-constexpr int kMaxBits = 12;        // bits of a bucket id (4096 buckets)
 
 struct WsLayout {
   int64_t nb, nc;
@@ -65,6 +64,9 @@ __device__ __forceinline__ int clamp_rank(const int32_t* src_rank, int64_t t, in
 // A: ranks inside (bucket, chunk) and per-chunk bucket counts
 // ---------------------------------------------------------------------------
 // Dynamic LDS: bucket[k][256] ints, then count[4 wavefronts][nb] ints.
+// KS >= k: slot loops are unrolled to KS (a power of two) with k as a guard,
+// so the per-lane state stays in registers and the code stays small.
+template <int KS>
 __global__ __launch_bounds__(kChunk) void permute_count_kernel(const int32_t* __restrict__ topk_idx,
                                                                const int32_t* __restrict__ src_rank, int64_t T,
                                                                int k, int expert_begin, int E_loc, int R, int nbits,
@@ -94,42 +96,42 @@ __global__ __launch_bounds__(kChunk) void permute_count_kernel(const int32_t* __
   // Rank of each of this lane's pairs among the wavefront's pairs with the same
   // bucket, and that bucket's count in the wavefront.  The other lanes' slot jp
   // is compared with all of this lane's slots at once: a lane matches when its
-  // bucket agrees on every bit, tested against one ballot per bit.  Rank (< 64)
-  // and count (<= 64) are packed into one int as rank | count << 16.
-  int packed[32];
+  // bucket agrees on every bit, one ballot per bit narrowing the KS candidate
+  // masks.  Rank (< 64) and count (<= 64) are packed into one int as
+  // rank | count << 16.
+  int own[KS], packed[KS];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) packed[j] = 0;
+  for (int j = 0; j < KS; ++j) {
+    own[j] = j < k ? s_bucket[j * kChunk + tid] : -1;
+    packed[j] = 0;
+  }
   for (int jp = 0; jp < k; ++jp) {
     const int bo = s_bucket[jp * kChunk + tid];
     const uint64_t vm = __ballot(bo >= 0);
-    uint64_t bits[kMaxBits];
+    uint64_t m[KS];
 #pragma unroll
-    for (int bit = 0; bit < kMaxBits; ++bit) bits[bit] = bit < nbits ? __ballot(bo >= 0 && ((bo >> bit) & 1)) : 0ull;
+    for (int j = 0; j < KS; ++j) m[j] = vm;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t bal = __ballot(bo >= 0 && ((bo >> bit) & 1));
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (j < k) {
-        const int b = s_bucket[j * kChunk + tid];
-        uint64_t m = vm;
-#pragma unroll
-        for (int bit = 0; bit < kMaxBits; ++bit)
-          if (bit < nbits) m &= ((b >> bit) & 1) ? bits[bit] : ~bits[bit];
-        packed[j] += (int)__popcll(m & below) | ((int)__popcll(m) << 16);
-      }
+      for (int j = 0; j < KS; ++j) m[j] &= ((own[j] >> bit) & 1) ? bal : ~bal;
     }
+#pragma unroll
+    for (int j = 0; j < KS; ++j) packed[j] += (int)__popcll(m[j] & below) | ((int)__popcll(m[j]) << 16);
   }
   // Each bucket present in this wavefront has exactly one pair with rank 0: it publishes the count.
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < KS; ++j) {
     if (j < k) {
-      const int b = s_bucket[j * kChunk + tid];
+      const int b = own[j];
       if (b >= 0 && (packed[j] & 0xFFFF) == 0) s_count[(int64_t)w * nb + b] = packed[j] >> 16;
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < KS; ++j) {
     if (j < k && valid) {
-      const int b = s_bucket[j * kChunk + tid];
+      const int b = own[j];
       int rk = -1;
       if (b >= 0) {
         rk = packed[j] & 0xFFFF;
@@ -375,13 +377,29 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   int nbits = 0;
   while ((1ll << nbits) < L.nb) ++nbits;
   const size_t count_lds = ((size_t)a.k * kChunk + 4 * (size_t)L.nb) * sizeof(int32_t);  // <= 96 KiB
+  const int ks = a.k <= 1 ? 1 : a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : a.k <= 16 ? 16 : 32;
+  const void* count_fn = ks == 1    ? reinterpret_cast<const void*>(permute_count_kernel<1>)
+                         : ks == 2  ? reinterpret_cast<const void*>(permute_count_kernel<2>)
+                         : ks == 4  ? reinterpret_cast<const void*>(permute_count_kernel<4>)
+                         : ks == 8  ? reinterpret_cast<const void*>(permute_count_kernel<8>)
+                         : ks == 16 ? reinterpret_cast<const void*>(permute_count_kernel<16>)
+                                    : reinterpret_cast<const void*>(permute_count_kernel<32>);
   if (count_lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_count_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)count_lds);
+    const hipError_t e = hipFuncSetAttribute(count_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)count_lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)L.nc), dim3(kChunk), count_lds, s, a.topk_idx, a.src_rank,
-                     a.T, a.k, a.expert_begin, a.E_loc, a.num_ranks, nbits, L.hist, L.lrank, L.nb, L.nc);
+#define MOE_COUNT(KS_)                                                                                           \
+  hipLaunchKernelGGL(permute_count_kernel<KS_>, dim3((unsigned)L.nc), dim3(kChunk), count_lds, s, a.topk_idx,  \
+                     a.src_rank, a.T, a.k, a.expert_begin, a.E_loc, a.num_ranks, nbits, L.hist, L.lrank, L.nb, L.nc)
+  switch (ks) {
+    case 1: MOE_COUNT(1); break;
+    case 2: MOE_COUNT(2); break;
+    case 4: MOE_COUNT(4); break;
+    case 8: MOE_COUNT(8); break;
+    case 16: MOE_COUNT(16); break;
+    default: MOE_COUNT(32); break;
+  }
+#undef MOE_COUNT
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, L.hist, L.nb, L.nc, a.E_loc,
                      a.num_ranks, a.tile_m, a.R_cap, a.tiles_cap, a.counts, a.offsets, a.row_src, a.tiles,
                      a.num_tiles);
