@@ -29,20 +29,26 @@
 //     inside a group, column block major then tile.  Layer1 order: column
 //     groups of kGroupN blocks (N-decomposition: a column group is finished
 //     for all tiles before the next starts); inside a group, tile major.
-//   * Operands are staged HBM -> LDS with direct-to-LDS loads (16 bytes per
-//     lane straight into LDS, no VGPR round trip: buffer_load_dwordx4 ... lds
-//     for big tiles, global_load_lds_dwordx4 for small ones) in a ring of
-//     STAGES buffers, BK = 64.  Each LDS row holds 64 bf16 (128 B) of one operand
-//     row; the 16-byte chunk index is XOR-swizzled with
-//     (row & 7) ^ ((row >> 3) & 1), so that the fragment reads (consecutive
-//     lanes read consecutive rows at one chunk) hit distinct banks both for
-//     8 lanes within 128 B and for 16 lanes within 256 B.
-//   * Big tiles: the loads of stage kt + STAGES - 1 are spread over the first
-//     K steps of stage kt, one after an MFMA, into the ring buffer freed at
-//     the previous barrier (a burst of them right after the barrier backs up
-//     the CU's address unit and stalls the issuing waves' matrix cores).
-//     Stages past the end load through a buffer resource with no records,
-//     so every iteration runs the same schedule.
+//   * Operands are staged HBM -> LDS in stages of BK = 64.  Each LDS row holds
+//     64 bf16 (128 B) of one operand row; the 16-byte chunk index is
+//     XOR-swizzled with (row & 7) ^ ((row >> 3) & 1), so that the fragment
+//     reads (consecutive lanes read consecutive rows at one chunk) hit
+//     distinct banks both for 8 lanes within 128 B and for 16 lanes within
+//     256 B.  Three load pipelines:
+//     - tile_m = 256 (two 64 KiB LDS stages fit): two LDS buffers and one
+//       register stage; iteration kt writes stage kt+1 from VGPRs into the
+//       free buffer while loading stage kt+2 into those VGPRs with plain
+//       16-byte buffer loads (the vector-load path moves more bytes per CU
+//       than direct-to-LDS loads when the operands stream from L2);
+//     - tile_m = 128: a ring of 3 LDS stages filled by direct-to-LDS loads
+//       (buffer_load_dwordx4 ... lds, no VGPR round trip);
+//     - small tiles: a ring of 4 LDS stages filled by global_load_lds, the
+//       weight rows loaded non-temporal.
+//   * Big tiles: the loads of a stage are spread over the first K steps of
+//     the previous one, one after an MFMA (a burst of them right after the
+//     barrier backs up the CU's address unit and stalls the issuing waves'
+//     matrix cores).  Stages past the end load through a buffer resource
+//     with no records, so every iteration runs the same schedule.
 //   * The stage boundary is software-pipelined: the wait for the next stage,
 //     the barrier and the next stage's first fragment reads are issued
 //     before the last MFMAs of the current stage, which keep the matrix
@@ -650,7 +656,8 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // Small-tile kernel (tile_m <= 64): WM x WN waves of v_mfma_f32_16x16x32_bf16,
-// double-buffered LDS.  These shapes stream weights from HBM.
+// a 4-stage LDS ring of direct-to-LDS loads (three stages in flight while one
+// is computed).  These shapes stream weights from HBM.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, bool DUAL, int EPI, int ORDER, bool GATHER>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
@@ -667,9 +674,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
   constexpr int TM = WT_M / 16, TN = WT_N / 16;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(BM % 8 == 0 && BROWS % 8 == 0, "rows per stage");
-  static_assert(!GATHER || BM / 8 <= NWAVES, "gathered rows: one 8-row group per wave");
+  static_assert(BM / 8 <= NWAVES, "token rows: at most one 8-row group per wave");
+  static_assert((BN / 8) % NWAVES == 0, "weight rows: the same number of 8-row groups on every wave");
+  // Ring of SR stages: SR - 1 stages of weights stream in while one is computed.
+  constexpr int SR = 4;
+  constexpr int LW_B = NMAT * (BN / 8 / NWAVES);  // direct-to-LDS loads per wave per stage (weights)
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[SR * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -683,13 +694,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
   const int nk = K / BK;
   const int64_t b_expert = (int64_t)N * K;
 
-  // rows per stage may not be a multiple of 8 * NWAVES: guard per 8-row group
-  auto stage_any = [&](const uint16_t* g, int rows, char* lds) {
+  // rows per stage may not be a multiple of 8 * NWAVES: guard per 8-row group.
+  // Weight rows are read once per launch at these shapes: they are loaded
+  // non-temporal (streaming), which lets a read-only stream run near the HBM
+  // peak instead of settling around 6 TB/s.
+  auto stage_any = [&](const uint16_t* g, int rows, char* lds, bool stream) {
     const int r_in = lane >> 3;
     for (int grp = wave; grp < rows / 8; grp += NWAVES) {
       const int chunk = (lane & 7) ^ swz(grp * 8 + r_in);
-      __builtin_amdgcn_global_load_lds(g + (int64_t)(grp * 8 + r_in) * K + chunk * 8, (lds_void*)(lds + grp * 1024),
-                                       16, 0, 0);
+      if (stream)
+        __builtin_amdgcn_global_load_lds(g + (int64_t)(grp * 8 + r_in) * K + chunk * 8, (lds_void*)(lds + grp * 1024),
+                                         16, 0, 2);
+      else
+        __builtin_amdgcn_global_load_lds(g + (int64_t)(grp * 8 + r_in) * K + chunk * 8, (lds_void*)(lds + grp * 1024),
+                                         16, 0, 0);
     }
   };
 
@@ -730,18 +748,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma16_kernel(
           __builtin_amdgcn_global_load_lds(a_row + k0 + ((lane & 7) ^ swz(wave * 8 + (lane >> 3))) * 8,
                                            (lds_void*)(s + wave * 1024), 16, 0, 0);
       } else {
-        stage_any(a_g + k0, BM, s);
+        stage_any(a_g + k0, BM, s, false);
       }
-      stage_any(b0_g + k0, BN, s + A_BYTES);
-      if (DUAL) stage_any(b1_g + k0, BN, s + A_BYTES + BN * 128);
+      stage_any(b0_g + k0, BN, s + A_BYTES, true);
+      if (DUAL) stage_any(b1_g + k0, BN, s + A_BYTES + BN * 128, true);
     };
 
-    issue(0, 0);
+    // Loads per wave per stage: the weight rows, plus one token-row group on
+    // the first BM / 8 waves.  Stage kt has landed once only the stages issued
+    // after it (at most SR - 2) are in flight.
+    const bool has_a = wave < BM / 8;
+#pragma unroll
+    for (int st = 0; st + 1 < SR; ++st)
+      if (st < nk) issue(st, st * BK);
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
-      const char* sA = smem + (kt & 1) * STAGE;
+      const int later = (nk - 1 - kt) < SR - 2 ? (nk - 1 - kt) : SR - 2;
+      if (has_a) {
+        if (later >= 2) wait_vmcnt<2 * (LW_B + 1)>();
+        else if (later == 1) wait_vmcnt<LW_B + 1>();
+        else wait_vmcnt<0>();
+      } else {
+        if (later >= 2) wait_vmcnt<2 * LW_B>();
+        else if (later == 1) wait_vmcnt<LW_B>();
+        else wait_vmcnt<0>();
+      }
+      wait_lgkm0();    // this wave's reads of stage kt - 1 are complete
+      ring_barrier();  // stage kt visible to all; buffer (kt - 1) % SR is free
+      if (kt + SR - 1 < nk) issue((kt + SR - 1) % SR, (kt + SR - 1) * BK);
+      const char* sA = smem + (kt % SR) * STAGE;
       const char* sB = sA + A_BYTES;
 #pragma unroll
       for (int ks = 0; ks < BK / 32; ++ks) {
