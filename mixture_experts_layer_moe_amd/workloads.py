@@ -235,7 +235,7 @@ CONFIGS: Dict[str, MoEConfig] = {
                     "8 experts top-2"),
     "fine_grained": MoEConfig(
         "fine_grained", T=8192, H=2048, F=1408, E=64, k=6, act="swiglu", logits="zipf",
-        tile_m=128,
+        tile_m=256,
         description="fine-grained MoE: 8192 tokens, hidden 2048, FFN 1408, SwiGLU, 64 experts "
                     "top-6, Zipf(1.1)-biased router"),
     "ep_share": MoEConfig(
