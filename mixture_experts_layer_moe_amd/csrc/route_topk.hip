@@ -10,21 +10,80 @@
 // so at most 16 per lane).  k rounds of a wave-wide arg-max on the key
 // (value desc, id asc) select the experts in slot order; the comparisons are
 // exact, so the ids are bit-identical to any correct sort with that key.
+// With E <= 64 (one logit per lane) a round is a wave-wide max (DPP inside
+// each 16-lane row, then two exchanges) and a ballot of the lanes holding
+// it: the lowest such lane is the lowest expert id among equal logits.
 #include "common.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
-
-constexpr int kMaxPerLane = 16;  // E <= 1024
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Wave-wide maximum, in every lane: quad swaps and the 8- and 16-lane mirrors
+// (DPP) give each lane its row's maximum, two exchanges combine the rows.
+__device__ __forceinline__ float wave_max(float x) {
+  auto perm = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  x = fmaxf(x, perm(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, perm(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, perm(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  x = fmaxf(x, perm(x, std::integral_constant<int, 0x140>{}));  // row_mirror
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// E <= 64: lane l holds logit l.
+__global__ __launch_bounds__(256) void route_topk_small_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                               int k, int renormalize,
+                                                               int32_t* __restrict__ topk_idx,
+                                                               float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+  const float x = lane < E ? logits[t * (int64_t)E + lane] : -__builtin_inff();
+  float v = x, top = 0.f, sel_v = 0.f, zsum = 0.f;
+  int sel_i = 0;
+  for (int j = 0; j < k; ++j) {
+    const float m = wave_max(v);
+    // k <= E and finite logits: some lane still holds m.
+    const int win = __builtin_ctzll(__ballot(v == m));
+    if (lane == win) v = -__builtin_inff();
+    if (j == 0) top = m;
+    zsum += expf(m - top);
+    if (lane == j) {
+      sel_v = m;
+      sel_i = win;
+    }
+  }
+  float denom = zsum;
+  if (!renormalize) {
+    // Full softmax denominator over all E logits.
+    float s = lane < E ? expf(x - top) : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    denom = s;
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = sel_i;
+    topk_w[t * k + lane] = expf(sel_v - top) / denom;
+  }
+}
+
+// General E (<= 64 * PL): lane l holds logits l, l + 64, ...
+template <int PL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int64_t T, int E, int k, int renormalize,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w) {
+  constexpr int kMaxPerLane = PL;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave exits together
@@ -100,8 +159,18 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int r
                              int32_t* topk_idx, float* topk_w, hipStream_t s) {
   constexpr int kTokensPerBlock = 4;
   const int64_t blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)blocks), dim3(kTokensPerBlock * kWave), 0, s,
-                     logits, T, E, k, renormalize, topk_idx, topk_w);
+  const dim3 grid((unsigned)blocks), block(kTokensPerBlock * kWave);
+  const int pl = (E + kWave - 1) / kWave;
+  if (pl <= 1)
+    hipLaunchKernelGGL(route_topk_small_kernel, grid, block, 0, s, logits, T, E, k, renormalize, topk_idx, topk_w);
+  else if (pl <= 2)
+    hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, renormalize, topk_idx, topk_w);
+  else if (pl <= 4)
+    hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, renormalize, topk_idx, topk_w);
+  else if (pl <= 8)
+    hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, renormalize, topk_idx, topk_w);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, renormalize, topk_idx, topk_w);
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ def test_route_full_size(dev, name):
     (200, 6, 6, "normal", True),          # k = E
     (257, 8, 2, "ties", True),            # many equal logits: lower id first
     (100, 65, 3, "ties", True),           # E not a multiple of the wave
+    (64, 64, 8, "ties", True),            # one logit per lane: ties broken by ballot, lowest lane
+    (50, 64, 4, "ties", False),           # same, full-softmax gate
     (64, 1024, 32, "normal", True),       # largest supported E and k
     (300, 16, 4, "normal", False),        # full-softmax weights
 ])
