@@ -21,7 +21,8 @@
 //               with 16-byte loads, per-expert counts, tile-padded offsets,
 //               padding markers in row_src, and the tile list ordered by
 //               (priority, expert, m-tile) with a stable partition on priority.
-//   D  scatter: one wavefront per token: row of each local pair =
+//   D  scatter: each block marks a slice of the unused rows past the last
+//               expert; one wavefront per token: row of each local pair =
 //               offsets[expert] + (prefix of its bucket and chunk - prefix of
 //               the expert) + rank in chunk, written to row_src / inv_perm, and
 //               the token's row copied once from HBM to each of its rows with
@@ -269,36 +270,66 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
   }
   __syncthreads();
 
-  // 3. padding rows and the unused tail carry -1 in row_src
+  // 3. padding rows carry -1 in row_src (the unused tail past the last expert
+  //    is marked by kernel D, spread over its blocks)
   for (int64_t i = tid; i < (int64_t)E_loc * tile_m; i += kScanThreads) {
     const int le = (int)(i / tile_m), q = (int)(i % tile_m);
     const int64_t row = (int64_t)s_off[le] + (s_us[le + 1] - s_us[le]) + q;
     if (row < s_off[le + 1]) row_src[row] = -1;
   }
-  for (int64_t row = (int64_t)s_off[E_loc] + tid; row < R_cap; row += kScanThreads) row_src[row] = -1;
 
   // 4. tile list, stably partitioned on priority (= rank of the tile's last row)
   const int nt = s_tb[E_loc] < tiles_cap ? s_tb[E_loc] : (int)tiles_cap;
   if (tid == 0) *num_tiles = nt;
+  // Tile i -> (expert le, m-tile m) by binary search in LDS; its priority
+  // from the expert's rank prefix in hist.  The priorities of the first
+  // kPrioChunks * kScanThreads tiles are computed once and kept in registers
+  // for the R partition passes; later tiles (if any) recompute theirs.
+  constexpr int kPrioChunks = 4;
+  auto tile_em = [&](int i, int& le, int& m) {
+    int a = 0, b = E_loc;  // largest le with s_tb[le] <= i
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (s_tb[mid] <= i) a = mid; else b = mid;
+    }
+    le = a;
+    m = i - s_tb[le];
+  };
+  auto tile_prio = [&](int le, int m) {
+    const int cnt = s_us[le + 1] - s_us[le];
+    const int last = ((m + 1) * tile_m < cnt ? (m + 1) * tile_m : cnt) - 1;
+    int prio = 0;
+    for (int r = 1; r < R; ++r) {
+      const int cum = hist[((int64_t)le * R + r) * nc] - s_us[le];  // rows of expert le with rank < r
+      if (cum <= last) prio = r;
+    }
+    return prio;
+  };
+  int cprio[kPrioChunks];
+#pragma unroll
+  for (int c = 0; c < kPrioChunks; ++c) {
+    const int i = c * kScanThreads + tid;
+    cprio[c] = 0;
+    if (R > 1 && i < nt) {
+      int le, m;
+      tile_em(i, le, m);
+      cprio[c] = tile_prio(le, m);
+    }
+  }
   int placed = 0;
   for (int p = 0; p < R; ++p) {
     for (int base_i = 0; base_i < nt; base_i += kScanThreads) {
       const int i = base_i + tid;
+      const int c = base_i / kScanThreads;
       int le = 0, prio = -1, m = 0;
       if (i < nt) {
-        int a = 0, b = E_loc;  // largest le with s_tb[le] <= i
-        while (b - a > 1) {
-          const int mid = (a + b) >> 1;
-          if (s_tb[mid] <= i) a = mid; else b = mid;
-        }
-        le = a;
-        m = i - s_tb[le];
-        const int cnt = s_us[le + 1] - s_us[le];
-        const int last = ((m + 1) * tile_m < cnt ? (m + 1) * tile_m : cnt) - 1;
-        prio = 0;
-        for (int r = 1; r < R; ++r) {
-          const int cum = hist[((int64_t)le * R + r) * nc] - s_us[le];  // rows of expert le with rank < r
-          if (cum <= last) prio = r;
+        tile_em(i, le, m);
+        if (c < kPrioChunks) {
+#pragma unroll
+          for (int cc = 0; cc < kPrioChunks; ++cc)
+            if (cc == c) prio = cprio[cc];
+        } else {
+          prio = tile_prio(le, m);
         }
       }
       const int flag = (prio == p) ? 1 : 0;
@@ -323,6 +354,12 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ lrank, int64_t nc, intx4* __restrict__ x_perm, int32_t* __restrict__ row_src,
     int32_t* __restrict__ inv_perm) {
   const int lane = threadIdx.x & 63;
+  {  // rows [offsets[E_loc], R_cap) are unused: -1 in row_src, a slice per block
+    const int64_t tail0 = offsets[E_loc], n = R_cap - tail0;
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = tail0 + (int64_t)blockIdx.x * per, hi = lo + per < R_cap ? lo + per : R_cap;
+    for (int64_t row = lo + threadIdx.x; row < hi; row += blockDim.x) row_src[row] = -1;
+  }
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave exits together
   int p = -1;

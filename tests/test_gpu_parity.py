@@ -144,6 +144,17 @@ def test_permute_tile_sizes_with_ranks(dev, tile_m):
     check_permute(d["x"], idx, d["src_rank"], cfg.E, 4, 6, 5, tile_m, dev)
 
 
+def test_permute_many_tiles_with_ranks(dev):
+    # More than 4096 tiles with source ranks: the scan kernel keeps the first 4096 tile priorities in
+    # registers across its priority passes and recomputes the rest; both must give the oracle's order.
+    cfg = W.MoEConfig("m", T=8300, H=64, F=128, E=64, k=8, act="swiglu", logits="normal",
+                      tile_m=16, num_ranks=4)
+    d = W.make_inputs(cfg, dev, weights=False)
+    idx, _ = P.oracle_route(d["logits"], cfg.k)
+    assert ffi.tiles_capacity(cfg.T, cfg.k, cfg.n_local, 16) > 4096
+    check_permute(d["x"], idx, d["src_rank"], cfg.E, 0, 64, 4, 16, dev)
+
+
 @pytest.mark.parametrize("case", ["one_token", "all_to_one_expert", "max_buckets", "k_equals_E",
                                   "no_local_pairs", "exact_tile_multiple"])
 def test_permute_edge_cases(dev, case):
