@@ -271,6 +271,16 @@ def test_grouped_ffn_gelu_ranks_and_ragged(dev, tile_m):
     check_grouped_ffn(cfg, tile_m, dev)
 
 
+@pytest.mark.parametrize("tile_m", TILE_MS)
+@pytest.mark.parametrize("H,F", [(128, 128), (128, 256), (256, 128)])
+def test_grouped_ffn_shortest_k(dev, tile_m, H, F):
+    # K of 128 or 256 is 2 or 4 stages of 64: shorter than the load pipelines (the register stage
+    # loads two stages ahead, the small-tile ring keeps three in flight), so their prologue and
+    # end-of-K handling run without a steady state in between.
+    cfg = W.MoEConfig("k", T=300, H=H, F=F, E=6, k=2, act="swiglu", logits="normal", tile_m=tile_m)
+    check_grouped_ffn(cfg, tile_m, dev)
+
+
 def test_grouped_ffn_zipf_uneven_experts(dev):
     cfg = W.CONFIGS["fine_grained"].with_(T=512, H=256, F=256)
     check_grouped_ffn(cfg, cfg.tile_m, dev)
