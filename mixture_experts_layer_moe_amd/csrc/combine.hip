@@ -19,15 +19,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 2;                      // float4 per thread
-constexpr int kCols = kThreads * kVec;       // float4 columns per block
 
-template <int K>
+// kVec float4 columns per thread (1, 2 or 4: a block covers up to a 4096-wide row).
+template <int K, int kVec>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const floatx4* __restrict__ y_perm,
                                                            const int32_t* __restrict__ inv_perm,
                                                            const float* __restrict__ topk_w, int k_rt,
                                                            int H4, int64_t R_cap,
                                                            floatx4* __restrict__ out) {
+  constexpr int kCols = kThreads * kVec;  // float4 columns per block
   const int kk = K > 0 ? K : k_rt;
   const int64_t t = blockIdx.x;
   const int c0 = blockIdx.y * kCols + threadIdx.x;
@@ -81,20 +81,32 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const floatx4* __rest
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T,
                           int k, int H, int64_t R_cap, float* out, hipStream_t s) {
   const int H4 = H / 4;
-  const dim3 grid((unsigned)T, (unsigned)((H4 + kCols - 1) / kCols));
   const floatx4* y = reinterpret_cast<const floatx4*>(y_perm);
   floatx4* o = reinterpret_cast<floatx4*>(out);
-#define MOE_COMBINE_CASE(KV) \
-  case KV: hipLaunchKernelGGL(combine_kernel<KV>, grid, dim3(kThreads), 0, s, y, inv_perm, topk_w, k, H4, R_cap, o); break;
-  switch (k) {
-    MOE_COMBINE_CASE(1)
-    MOE_COMBINE_CASE(2)
-    MOE_COMBINE_CASE(4)
-    MOE_COMBINE_CASE(6)
-    MOE_COMBINE_CASE(8)
-    default: hipLaunchKernelGGL(combine_kernel<0>, grid, dim3(kThreads), 0, s, y, inv_perm, topk_w, k, H4, R_cap, o);
+  // Float4 columns per thread: enough that one block covers the row (up to 4),
+  // so a token's index and weight loads are paid once.
+  const int vec = H4 >= 4 * kThreads ? 4 : H4 >= 2 * kThreads ? 2 : 1;
+#define MOE_COMBINE_LAUNCH(KV, V)                                                                              \
+  hipLaunchKernelGGL((combine_kernel<KV, V>), dim3((unsigned)T, (unsigned)((H4 + kThreads * V - 1) / (kThreads * V))), \
+                     dim3(kThreads), 0, s, y, inv_perm, topk_w, k, H4, R_cap, o)
+#define MOE_COMBINE_V(V)                                  \
+  switch (k) {                                            \
+    case 1: MOE_COMBINE_LAUNCH(1, V); break;              \
+    case 2: MOE_COMBINE_LAUNCH(2, V); break;              \
+    case 4: MOE_COMBINE_LAUNCH(4, V); break;              \
+    case 6: MOE_COMBINE_LAUNCH(6, V); break;              \
+    case 8: MOE_COMBINE_LAUNCH(8, V); break;              \
+    default: MOE_COMBINE_LAUNCH(0, V); break;             \
   }
-#undef MOE_COMBINE_CASE
+  if (vec == 4) {
+    MOE_COMBINE_V(4)
+  } else if (vec == 2) {
+    MOE_COMBINE_V(2)
+  } else {
+    MOE_COMBINE_V(1)
+  }
+#undef MOE_COMBINE_V
+#undef MOE_COMBINE_LAUNCH
   return hipGetLastError();
 }
 
