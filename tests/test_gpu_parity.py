@@ -145,7 +145,7 @@ def test_permute_tile_sizes_with_ranks(dev, tile_m):
 
 
 def test_permute_many_tiles_with_ranks(dev):
-    # More than 4096 tiles with source ranks: the scan kernel keeps the first 4096 tile priorities in
+    # More than 4096 tiles with source ranks: the tile-list pass keeps the first 4096 tile priorities in
     # registers across its priority passes and recomputes the rest; both must give the oracle's order.
     cfg = W.MoEConfig("m", T=8300, H=64, F=128, E=64, k=8, act="swiglu", logits="normal",
                       tile_m=16, num_ranks=4)
@@ -153,6 +153,18 @@ def test_permute_many_tiles_with_ranks(dev):
     idx, _ = P.oracle_route(d["logits"], cfg.k)
     assert ffi.tiles_capacity(cfg.T, cfg.k, cfg.n_local, 16) > 4096
     check_permute(d["x"], idx, d["src_rank"], cfg.E, 0, 64, 4, 16, dev)
+
+
+def test_permute_large_histogram(dev):
+    # 512 (expert, rank) buckets x 67 chunks of 256 tokens: too many per-chunk counts to copy into every
+    # placing block, so the single-block scan runs between the count and place launches.
+    cfg = W.MoEConfig("m", T=17000, H=64, F=128, E=64, k=4, act="swiglu", logits="normal",
+                      tile_m=32, num_ranks=8)
+    d = W.make_inputs(cfg, dev, weights=False)
+    idx, _ = P.oracle_route(d["logits"], cfg.k)
+    nb, nc = 64 * 8, (cfg.T + 255) // 256
+    assert nc * nb * nc > 1 << 21
+    check_permute(d["x"], idx, d["src_rank"], cfg.E, 0, 64, 8, 32, dev)
 
 
 @pytest.mark.parametrize("case", ["one_token", "all_to_one_expert", "max_buckets", "k_equals_E",
