@@ -10,9 +10,11 @@
 // so at most 16 per lane).  k rounds of a wave-wide arg-max on the key
 // (value desc, id asc) select the experts in slot order; the comparisons are
 // exact, so the ids are bit-identical to any correct sort with that key.
-// With E <= 64 (one logit per lane) a round is a wave-wide max (DPP inside
-// each 16-lane row, then two exchanges) and a ballot of the lanes holding
-// it: the lowest such lane is the lowest expert id among equal logits.
+// A round is a wave-wide max of the lanes' best logits (DPP inside each
+// 16-lane row, then the four row results by readlane).  With E <= 64 (one
+// logit per lane) a ballot of the lanes holding it follows: the lowest such
+// lane is the lowest expert id among equal logits; otherwise a wave-wide
+// minimum of the ids of the lanes holding it.
 #include "common.h"
 
 #include <type_traits>
@@ -24,20 +26,36 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// Wave-wide maximum, in every lane: quad swaps and the 8- and 16-lane mirrors
-// (DPP) give each lane its row's maximum, two exchanges combine the rows.
+// Wave-wide reductions, result in every lane: quad swaps and the 8- and
+// 16-lane mirrors (DPP) give each lane its 16-lane row's result, and the four
+// row results are read with readlane (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lanef(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-  auto perm = [](float v, auto ctrl) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                                                 decltype(ctrl)::value, 0xF, 0xF, false));
-  };
-  x = fmaxf(x, perm(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, perm(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, perm(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
-  x = fmaxf(x, perm(x, std::integral_constant<int, 0x140>{}));  // row_mirror
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+  return fmaxf(fmaxf(lanef(x, 0), lanef(x, 16)), fmaxf(lanef(x, 32), lanef(x, 48)));
+}
+
+__device__ __forceinline__ int wave_min(int x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  x = min(x, dpp<0x140>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // E <= 64: lane l holds logit l.
@@ -115,15 +133,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         bi = lane + i * kWave;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    // Wave arg-max on (value desc, id asc): the largest value, then the lowest id holding it.
+    const float m = wave_max(bv);
+    bi = wave_min(bv == m ? bi : 0x7fffffff);
+    bv = m;
     // bv, bi are now wave-uniform: the j-th expert of this token.
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (j == 0) top = bv;
