@@ -44,10 +44,10 @@
 //       (buffer_load_dwordx4 ... lds, no VGPR round trip);
 //     - small tiles: a ring of 4 LDS stages filled by global_load_lds, the
 //       weight rows loaded non-temporal.
-//   * Big tiles: the loads of a stage are spread over the first K steps of
-//     the previous one, one after an MFMA (a burst of them right after the
-//     barrier backs up the CU's address unit and stalls the issuing waves'
-//     matrix cores).  Stages past the end load through a buffer resource
+//   * Big tiles: the loads of a stage are spread evenly over the K steps of
+//     the previous one but its last, between MFMAs (a burst of them right
+//     after the barrier backs up the CU's address unit and stalls the issuing
+//     waves' matrix cores).  Stages past the end load through a buffer resource
 //     with no records, so every iteration runs the same schedule.
 //   * The stage boundary is software-pipelined: the wait for the next stage,
 //     the barrier and the next stage's first fragment reads are issued
@@ -318,11 +318,12 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
   constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
 
-  // Loads of one stage are spread over the first SPREAD K steps of the
-  // previous stage, one after every other MFMA: issued in one burst they back
-  // up the CU's address unit, which stalls the issuing waves (and with them
-  // their matrix cores) for a large part of the stage.
-  constexpr int SPREAD = (2 * LOADS + NMFMA - 1) / NMFMA < BK / 16 - 1 ? (2 * LOADS + NMFMA - 1) / NMFMA : BK / 16 - 1;
+  // Loads of one stage are spread evenly over the K steps of the previous
+  // stage but its last (which straddles the stage barrier): issued in one
+  // burst they back up the CU's address unit, which stalls the issuing waves
+  // (and with them their matrix cores) for a large part of the stage, and a
+  // smoother request stream also lowers their latency from L2.
+  constexpr int SPREAD = BK / 16 - 1;
   constexpr int PER_STEP = (LOADS + SPREAD - 1) / SPREAD;
 
 // K steps of one stage but the last: the next step's fragments are read
