@@ -45,9 +45,9 @@
 //     - small tiles: a ring of 4 LDS stages filled by global_load_lds, the
 //       weight rows loaded non-temporal.
 //   * Big tiles: the loads of a stage are spread evenly over the K steps of
-//     the previous one but its last, between MFMAs (a burst of them right
-//     after the barrier backs up the CU's address unit and stalls the issuing
-//     waves' matrix cores).  Stages past the end load through a buffer resource
+//     the previous one, between MFMAs (a burst of them right after the
+//     barrier backs up the CU's address unit and stalls the issuing waves'
+//     matrix cores; a smooth request stream also sees lower L2 latency).  Stages past the end load through a buffer resource
 //     with no records, so every iteration runs the same schedule.
 //   * The stage boundary is software-pipelined: the wait for the next stage,
 //     the barrier and the next stage's first fragment reads are issued
@@ -318,11 +318,12 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int NMFMA = NMAT * TN * TM;   // MFMAs per 16-wide K step
   constexpr int NREAD = TM + NMAT * TN;   // fragment reads per 16-wide K step
 
-  // Loads of one stage are spread evenly over the K steps of the previous
-  // stage but its last (which straddles the stage barrier): issued in one
-  // burst they back up the CU's address unit, which stalls the issuing waves
-  // (and with them their matrix cores) for a large part of the stage, and a
-  // smoother request stream also lowers their latency from L2.
+  // Direct-to-LDS ring: the loads of one stage are spread evenly over the K
+  // steps of the previous stage but its last (which straddles the stage
+  // barrier): issued in one burst they back up the CU's address unit, which
+  // stalls the issuing waves (and with them their matrix cores) for a large
+  // part of the stage, and a smoother request stream also lowers their
+  // latency from L2.
   constexpr int SPREAD = BK / 16 - 1;
   constexpr int PER_STEP = (LOADS + SPREAD - 1) / SPREAD;
 
@@ -369,6 +370,11 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   // L2.  Load p of a stage goes to the same LDS place as the direct-to-LDS
   // load p would, so the fragment reads are shared with the ring below.
   u32x4 stg[LOADS];
+  // The loads of a stage are spread evenly over all four K steps of the
+  // previous one: PSV per step, NPL of them in the step that straddles the
+  // stage barrier (issued with its first half of MFMAs, before the wait).
+  constexpr int PSV = (LOADS + BK / 16 - 1) / (BK / 16);
+  constexpr int NPL = LOADS - (BK / 16 - 1) * PSV > 0 ? LOADS - (BK / 16 - 1) * PSV : 0;
   auto vload = [&](int p, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0, __amdgpu_buffer_rsrc_t b1,
                    uint32_t vo) {
     const bool is_a = p < A_PIECES;
@@ -394,17 +400,17 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   ring_barrier();
   cur = read_frags(0, 0);
 // K steps of one stage but the last: the next step's fragments are read
-// from BUF while this step's MFMAs issue; steps below SPREAD also write their
-// share of the registers into WBUF and reload them from K offset KN through
+// from BUF while this step's MFMAs issue; each step also writes its share of
+// the registers into WBUF and reloads them from K offset KN through
 // (RA, RB0, RB1), each write before the load that reuses its registers.
 #define MOE_INNER_STEPS_VL(BUF, WBUF, KN, RA, RB0, RB1)                               \
   _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {                        \
-  const int np_ = ks < SPREAD ? (LOADS - ks * PER_STEP < PER_STEP ? LOADS - ks * PER_STEP : PER_STEP) : 0; \
+  const int np_ = LOADS - ks * PSV < PSV ? LOADS - ks * PSV : PSV;                  \
   Frags nxt;                                                                        \
   _Pragma("unroll") for (int t = 0; t < NREAD; ++t) read_one(nxt, (BUF), ks + 1, t); \
   _Pragma("unroll") for (int t = 0; t < np_; ++t) {                                 \
-    vwrite(ks * PER_STEP + t, (WBUF));                                              \
-    vload(ks * PER_STEP + t, (KN), (RA), (RB0), (RB1), MOE_VOFF(ks * PER_STEP + t)); \
+    vwrite(ks * PSV + t, (WBUF));                                                   \
+    vload(ks * PSV + t, (KN), (RA), (RB0), (RB1), MOE_VOFF(ks * PSV + t));          \
   }                                                                                 \
   MOE_MFMAS(cur, 0, NMFMA)                                                          \
   if (np_ > 0)                                                                      \
@@ -429,7 +435,28 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
     const int buf = kt & 1, wbuf = buf ^ 1;
     const bool real = kt + 2 < nk;
     MOE_INNER_STEPS_VL(buf, wbuf, (kt + 2) * BK, real ? ra : rnone, real ? rb0 : rnone, real ? rb1 : rnone)
+    constexpr int P0 = (BK / 16 - 1) * PSV;
+#pragma unroll
+    for (int t = 0; t < NPL; ++t) {
+      vwrite(P0 + t, wbuf);
+      vload(P0 + t, (kt + 2) * BK, real ? ra : rnone, real ? rb0 : rnone, real ? rb1 : rnone, MOE_VOFF(P0 + t));
+    }
     MOE_MFMAS(cur, 0, NMFMA / 2)
+    if (NPL > 0)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i) asm volatile("" : "+a"(acc[m][j][i]));
+#pragma unroll
+    for (int t = 0; t < NMFMA / 2 || t < 2 * NPL; ++t) {
+      if (t < NMFMA / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t < 2 * NPL) {
+        if (t % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkm0();     // this wave's reads of stage kt and writes of stage kt+1 are complete
     ring_barrier();   // stage kt+1 visible to all; buffer kt % 2 is free from the next iteration on
