@@ -80,8 +80,11 @@ def test_route_full_size(dev, name):
     (200, 6, 6, "normal", True),          # k = E
     (257, 8, 2, "ties", True),            # many equal logits: lower id first
     (100, 65, 3, "ties", True),           # E not a multiple of the wave
-    (64, 64, 8, "ties", True),            # one logit per lane: ties broken by ballot, lowest lane
+    (64, 64, 8, "ties", True),            # four lanes per token (E <= 64, k <= 8): merged top-k lists
     (50, 64, 4, "ties", False),           # same, full-softmax gate
+    (300, 50, 5, "ties", True),           # E not a multiple of 4: scalar logit loads
+    (70, 64, 12, "ties", True),           # k > 8 with E <= 64: one logit per lane, ballot tie-break
+    (33, 17, 9, "normal", False),         # same, full-softmax gate
     (64, 1024, 32, "normal", True),       # largest supported E and k
     (300, 16, 4, "normal", False),        # full-softmax weights
 ])
