@@ -51,7 +51,7 @@ struct WsLayout {
 
 __host__ __device__ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-__host__ __device__ inline WsLayout ws_layout(void* ws, int64_t T, int k, int E_loc, int num_ranks) {
+__host__ __device__ inline WsLayout ws_layout(void* ws, int64_t T, int E_loc, int num_ranks) {
   WsLayout L;
   L.nb = (int64_t)E_loc * num_ranks;
   L.nc = (T + kChunk - 1) / kChunk;
@@ -494,7 +494,7 @@ size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks) {
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  WsLayout L = ws_layout(a.ws, a.T, a.k, a.E_loc, a.num_ranks);
+  WsLayout L = ws_layout(a.ws, a.T, a.E_loc, a.num_ranks);
   const size_t count_lds = 4 * (size_t)L.nb * sizeof(unsigned long long);  // <= 128 KiB
   const int ks = a.k <= 1 ? 1 : a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : a.k <= 16 ? 16 : 32;
   const void* count_fn = ks == 1    ? reinterpret_cast<const void*>(permute_count_kernel<1>)
