@@ -35,11 +35,13 @@
 //     reads (consecutive lanes read consecutive rows at one chunk) hit
 //     distinct banks both for 8 lanes within 128 B and for 16 lanes within
 //     256 B.  Three load pipelines:
-//     - tile_m = 256 (two 64 KiB LDS stages fit): two LDS buffers and one
-//       register stage; iteration kt writes stage kt+1 from VGPRs into the
-//       free buffer while loading stage kt+2 into those VGPRs with plain
-//       16-byte buffer loads (the vector-load path moves more bytes per CU
-//       than direct-to-LDS loads when the operands stream from L2);
+//     - tile_m = 256 (two 64 KiB LDS stages fit): two LDS buffers and
+//       register staging; iteration kt writes stage kt+1 from VGPRs into the
+//       free buffer while loading the token rows of stage kt+2 and the weight
+//       rows of stage kt+3 (two register sets by stage parity) into those
+//       VGPRs with plain 16-byte buffer loads (the vector-load path moves
+//       more bytes per CU than direct-to-LDS loads when the operands stream
+//       from L2);
 //     - tile_m = 128: a ring of 3 LDS stages filled by direct-to-LDS loads
 //       (buffer_load_dwordx4 ... lds, no VGPR round trip);
 //     - small tiles: a ring of 4 LDS stages filled by global_load_lds, the
@@ -73,6 +75,8 @@
 //   * Token rows past an expert's real count read as zeros (out-of-range
 //     buffer offsets): they fetch nothing and their MFMAs multiply zeros.
 #include "common.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -361,57 +365,64 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   }
   Frags cur;
   if constexpr (STAGES == 2) {
-  // Two LDS buffers and one register stage: iteration kt computes stage kt
-  // from buffer kt % 2 while it writes stage kt+1, which arrived in
-  // registers during iteration kt-1, into the other buffer and loads stage
-  // kt+2 into those registers.  A load has a whole K stage to land, its
-  // LDS write is spread over the MFMAs, and the plain vector loads move
-  // more bytes per CU than direct-to-LDS ones when the tile streams from
-  // L2.  Load p of a stage goes to the same LDS place as the direct-to-LDS
-  // load p would, so the fragment reads are shared with the ring below.
-  u32x4 stg[LOADS];
-  // The loads of a stage are spread evenly over all four K steps of the
-  // previous one: PSV per step, NPL of them in the step that straddles the
-  // stage barrier (issued with its first half of MFMAs, before the wait).
+  // Two LDS buffers and register-staged loads: iteration kt computes stage
+  // kt from buffer kt % 2 while it writes stage kt+1, which arrived in
+  // registers earlier, into the other buffer.  Token rows are then reloaded
+  // with stage kt+2 (one register set: a whole K stage to land); weight rows,
+  // which mostly come from HBM rather than the last-level cache, alternate
+  // between two register sets by stage parity and are reloaded with stage
+  // kt+3 (two K stages to land).  The LDS writes are spread over the MFMAs,
+  // and the plain vector loads move more bytes per CU than direct-to-LDS
+  // ones when the tile streams from L2.  Load p of a stage goes to the same
+  // LDS place as the direct-to-LDS load p would, so the fragment reads are
+  // shared with the ring below.
+  constexpr int WP = LOADS - A_PIECES;
+  u32x4 stga[A_PIECES > 0 ? A_PIECES : 1];
+  u32x4 stgw[2][WP];
   constexpr int PSV = (LOADS + BK / 16 - 1) / (BK / 16);
   constexpr int NPL = LOADS - (BK / 16 - 1) * PSV > 0 ? LOADS - (BK / 16 - 1) * PSV : 0;
-  auto vload = [&](int p, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0, __amdgpu_buffer_rsrc_t b1,
-                   uint32_t vo) {
+  auto vload = [&](int p, int set, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0,
+                   __amdgpu_buffer_rsrc_t b1, uint32_t vo) {
     const bool is_a = p < A_PIECES;
     const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
-    stg[p] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? a : (m ? b1 : b0), vo,
-                                                   ((is_a ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(is_a ? a : (m ? b1 : b0), vo,
+                                                          ((is_a ? 0 : q * 8 * NWAVES * K) + k_begin + k0) * 2, 0);
+    if (is_a) stga[p] = v; else stgw[set][pb] = v;
   };
-  auto vwrite = [&](int p, int buf) {
+  auto vwrite = [&](int p, int set, int buf) {
     const bool is_a = p < A_PIECES;
     const int pb = is_a ? 0 : p - A_PIECES, m = pb / B_PIECES, q = is_a ? p : pb % B_PIECES;
     const int lds_off = (is_a ? 0 : A_BYTES + m * BN * 128) + (q * NWAVES + wave) * 1024;
-    *reinterpret_cast<u32x4*>(smem + buf * STAGE + lds_off + lane * 16) = stg[p];
+    *reinterpret_cast<u32x4*>(smem + buf * STAGE + lds_off + lane * 16) = is_a ? stga[p] : stgw[set][pb];
   };
-  // Prologue: stage 0 into buffer 0, stage 1 into the registers.
+  // Prologue: stage 0 into buffer 0, stage 1 into the registers (weights: set 1), stage 2's weights into set 0.
 #pragma unroll
-  for (int p = 0; p < LOADS; ++p) vload(p, 0, ra, rb0, rb1, MOE_VOFF(p));
+  for (int p = 0; p < LOADS; ++p) vload(p, 0, 0, ra, rb0, rb1, MOE_VOFF(p));
 #pragma unroll
-  for (int p = 0; p < LOADS; ++p) vwrite(p, 0);
+  for (int p = 0; p < LOADS; ++p) vwrite(p, 0, 0);
 #pragma unroll
   for (int p = 0; p < LOADS; ++p)
-    vload(p, BK, 1 < nk ? ra : rnone, 1 < nk ? rb0 : rnone, 1 < nk ? rb1 : rnone, MOE_VOFF(p));
+    vload(p, 1, BK, 1 < nk ? ra : rnone, 1 < nk ? rb0 : rnone, 1 < nk ? rb1 : rnone, MOE_VOFF(p));
+#pragma unroll
+  for (int p = A_PIECES; p < LOADS; ++p) vload(p, 0, 2 * BK, ra, 2 < nk ? rb0 : rnone, 2 < nk ? rb1 : rnone, voff);
   wait_lgkm0();
   ring_barrier();
   cur = read_frags(0, 0);
-// K steps of one stage but the last: the next step's fragments are read
-// from BUF while this step's MFMAs issue; each step also writes its share of
-// the registers into WBUF and reloads them from K offset KN through
-// (RA, RB0, RB1), each write before the load that reuses its registers.
-#define MOE_INNER_STEPS_VL(BUF, WBUF, KN, RA, RB0, RB1)                               \
+  // Piece p of stage kt+1 goes from registers to LDS buffer WB (weights from set WB, the parity of kt+1), then
+  // its registers reload: tokens stage kt+2 through (RA, RB0, RB1), weights stage kt+3 through (RB0W, RB1W).
+  auto piece = [&](int p, int wb, int kt, __amdgpu_buffer_rsrc_t RA, __amdgpu_buffer_rsrc_t RB0,
+                   __amdgpu_buffer_rsrc_t RB1, __amdgpu_buffer_rsrc_t RB0W, __amdgpu_buffer_rsrc_t RB1W) {
+    vwrite(p, wb, wb);
+    if (p < A_PIECES) vload(p, wb, (kt + 2) * BK, RA, RB0, RB1, MOE_VOFF(p));
+    else vload(p, wb, (kt + 3) * BK, RA, RB0W, RB1W, MOE_VOFF(p));
+  };
+#define MOE_INNER_STEPS_VL(BUF, WBUF, KT, RA, RB0, RB1, RB0W, RB1W)                    \
   _Pragma("unroll") for (int ks = 0; ks + 1 < BK / 16; ++ks) {                        \
   const int np_ = LOADS - ks * PSV < PSV ? LOADS - ks * PSV : PSV;                  \
   Frags nxt;                                                                        \
   _Pragma("unroll") for (int t = 0; t < NREAD; ++t) read_one(nxt, (BUF), ks + 1, t); \
-  _Pragma("unroll") for (int t = 0; t < np_; ++t) {                                 \
-    vwrite(ks * PSV + t, (WBUF));                                                   \
-    vload(ks * PSV + t, (KN), (RA), (RB0), (RB1), MOE_VOFF(ks * PSV + t));          \
-  }                                                                                 \
+  _Pragma("unroll") for (int t = 0; t < np_; ++t)                                   \
+    piece(ks * PSV + t, (WBUF), (KT), (RA), (RB0), (RB1), (RB0W), (RB1W));          \
   MOE_MFMAS(cur, 0, NMFMA)                                                          \
   if (np_ > 0)                                                                      \
   _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                  \
@@ -428,19 +439,16 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   __builtin_amdgcn_sched_barrier(0);                                                \
   cur = nxt;                                                                        \
   }
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    // Buffer wbuf held stage kt-1, which every wave finished reading before
-    // the barrier that ended iteration kt-1.  A stage past the end is loaded
-    // through resources with no records (zeros, nothing fetched).
-    const int buf = kt & 1, wbuf = buf ^ 1;
-    const bool real = kt + 2 < nk;
-    MOE_INNER_STEPS_VL(buf, wbuf, (kt + 2) * BK, real ? ra : rnone, real ? rb0 : rnone, real ? rb1 : rnone)
+  // Iteration kt with parity PAR (a constant): computes stage kt from buffer PAR.
+  auto iter = [&](auto par, int kt) {
+    constexpr int buf = decltype(par)::value, wbuf = buf ^ 1;
+    const bool real = kt + 2 < nk, real3 = kt + 3 < nk;
+    const __amdgpu_buffer_rsrc_t RA = real ? ra : rnone, RB0 = real ? rb0 : rnone, RB1 = real ? rb1 : rnone;
+    const __amdgpu_buffer_rsrc_t RB0W = real3 ? rb0 : rnone, RB1W = real3 ? rb1 : rnone;
+    MOE_INNER_STEPS_VL(buf, wbuf, kt, RA, RB0, RB1, RB0W, RB1W)
     constexpr int P0 = (BK / 16 - 1) * PSV;
 #pragma unroll
-    for (int t = 0; t < NPL; ++t) {
-      vwrite(P0 + t, wbuf);
-      vload(P0 + t, (kt + 2) * BK, real ? ra : rnone, real ? rb0 : rnone, real ? rb1 : rnone, MOE_VOFF(P0 + t));
-    }
+    for (int t = 0; t < NPL; ++t) piece(P0 + t, wbuf, kt, RA, RB0, RB1, RB0W, RB1W);
     MOE_MFMAS(cur, 0, NMFMA / 2)
     if (NPL > 0)
 #pragma unroll
@@ -465,7 +473,13 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
     MOE_MFMAS(cur, NMFMA / 2, NMFMA - NMFMA / 2)
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    iter(std::integral_constant<int, 0>{}, kt);
+    iter(std::integral_constant<int, 1>{}, kt + 1);
   }
+  if (kt + 1 < nk) iter(std::integral_constant<int, 0>{}, kt);
 #undef MOE_INNER_STEPS_VL
   } else {
   // STAGES-deep ring of direct-to-LDS loads: the prologue loads stages 0 .. STAGES-2; iteration kt
