@@ -475,6 +475,45 @@ def test_tensor_parallel_partials_sum_to_full_layer(dev):
     assert err <= 1e-5 * f.abs().max().item()
 
 
+@pytest.mark.parametrize("tile_m", [64, 256])
+def test_expert_parallel_shares_sum_to_full_layer(dev, tile_m):
+    # Expert parallelism on one GPU: each of 4 ranks runs the layer over its own 2 of the 8 experts
+    # (the tokens' other slots are not local to it); the rank outputs sum to the full layer's.  A
+    # rank's rows are the full layer's rows of its experts, so their activations agree bitwise and
+    # the sum differs from the full output only by the fp32 order of the top-k reduce.  With 256-row
+    # tiles the last scheduling round of each GEMM is split along K and summed in another fp32
+    # order, and which items fall in that round differs between a rank and the full layer: there an
+    # activation may differ by a bf16 ulp (or by fp32 noise near zero), and the outputs by what such
+    # flips carry through W1.
+    cfg = W.CONFIGS["mixtral"].with_(T=1024, H=256, F=512, tile_m=tile_m)
+    split = tile_m >= 128
+    full = MoELayer.from_inputs(cfg, W.make_inputs(cfg, dev))
+    full.run()
+    full_inv = full.perm.inv_perm.reshape(-1)
+    parts = []
+    for r in range(4):
+        c = cfg.with_(expert_begin=2 * r, E_loc=2)
+        lay = MoELayer.from_inputs(c, W.make_inputs(c, dev))
+        lay.run()
+        torch.cuda.synchronize()
+        real = (lay.perm.row_src >= 0).nonzero().squeeze(1)
+        full_rows = full_inv[lay.perm.row_src[real].long()].long()
+        a, b = lay.act_buf[real], full.act_buf[full_rows]
+        if split:
+            # an ulp of the larger magnitude, plus an absolute floor for activations near zero
+            af, bf = a.float(), b.float()
+            assert torch.all((af - bf).abs() <= torch.maximum(af.abs(), bf.abs()) * 2.0 ** -7 + 1e-5)
+        else:
+            assert torch.equal(bits16(a), bits16(b))
+        parts.append(lay.out.clone())
+    torch.cuda.synchronize()
+    f = full.out
+    err = (sum(parts) - f).abs().max().item()
+    print(f"[parity] ep=4 share sum vs full layer (tile_m {tile_m}): max |err| {err:.3e}, "
+          f"max |out| {f.abs().max().item():.3e}")
+    assert err <= (2e-3 if split else 1e-5) * f.abs().max().item()
+
+
 @pytest.mark.parametrize("name,over", [
     ("mixtral", {}),
     # GELU (one layer0 matrix): 35 row tiles x 32 column blocks = 1120 layer0 items, 96 left for the last round
