@@ -379,6 +379,9 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   constexpr int WP = LOADS - A_PIECES;
   u32x4 stga[A_PIECES > 0 ? A_PIECES : 1];
   u32x4 stgw[2][WP];
+  // The writes and loads of a stage are spread evenly over all four K steps
+  // of the previous one: PSV per step, NPL of them in the step that straddles
+  // the stage barrier (issued with its first half of MFMAs, before the wait).
   constexpr int PSV = (LOADS + BK / 16 - 1) / (BK / 16);
   constexpr int NPL = LOADS - (BK / 16 - 1) * PSV > 0 ? LOADS - (BK / 16 - 1) * PSV : 0;
   auto vload = [&](int p, int set, int k0, __amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b0,
@@ -439,7 +442,7 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
   __builtin_amdgcn_sched_barrier(0);                                                \
   cur = nxt;                                                                        \
   }
-  // Iteration kt with parity PAR (a constant): computes stage kt from buffer PAR.
+  // Iteration kt, whose parity is the constant `par`: computes stage kt from buffer par.
   auto iter = [&](auto par, int kt) {
     constexpr int buf = decltype(par)::value, wbuf = buf ^ 1;
     const bool real = kt + 2 < nk, real3 = kt + 3 < nk;
