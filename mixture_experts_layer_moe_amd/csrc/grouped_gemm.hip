@@ -49,8 +49,9 @@
 //   * Big tiles: the loads of a stage are spread evenly over the K steps of
 //     the previous one, between MFMAs (a burst of them right after the
 //     barrier backs up the CU's address unit and stalls the issuing waves'
-//     matrix cores; a smooth request stream also sees lower L2 latency).  Stages past the end load through a buffer resource
-//     with no records, so every iteration runs the same schedule.
+//     matrix cores; a smooth request stream also sees lower L2 latency).
+//     Stages past the end load through a buffer resource with no records,
+//     so every iteration runs the same schedule.
 //   * The stage boundary is software-pipelined: the wait for the next stage,
 //     the barrier and the next stage's first fragment reads are issued
 //     before the last MFMAs of the current stage, which keep the matrix
