@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null pointer, misalignment, negative or inconsistent size */
-  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement (e.g. H % 64) */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement (e.g. moe_grouped_ffn with H % 128 != 0) */
   MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_permute_workspace_bytes() */
   MOE_ERR_LAUNCH = 4       /* the HIP runtime reported an error when launching */
 } moe_status;
@@ -150,6 +150,12 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
  *   w0      [E_loc, F, H] bf16: W_gate^T (SwiGLU) or W1^T (GELU)
  *   w0_up   [E_loc, F, H] bf16: W_up^T (SwiGLU); must be NULL for GELU
  *   w1      [E_loc, H, F] bf16: W_down^T (SwiGLU) or W2^T (GELU)
+ * This is not the input-major layout a literal reading of "W1 H x F" gives
+ * ([E_loc, H, F] for w0 and [E_loc, F, H] for w1): with K contiguous in both
+ * GEMM operands, every operand row is one 128-byte LDS row per 64-wide K
+ * stage and the MFMA fragments are read without a transpose (the storage of
+ * a torch Linear weight).  A caller holding input-major weights transposes
+ * them once, at load time.
  *   act_buf [R_cap, F] bf16 out: the activation, rounded to nearest even.
  *   y_perm  [R_cap, H] fp32 out.
  * Only real rows are written; padding rows of act_buf and y_perm are left
@@ -163,8 +169,9 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
  * activation), so the result stays deterministic; it can differ from the
  * result without ws by fp32 summation order (layer0: by an ulp of the bf16
  * activation).  A non-NULL ws that is too small returns MOE_ERR_WORKSPACE.
- * Requires H % 128 == 0, F % 128 == 0, H <= 1048576, F <= 1048576,
- * tile_m in {16, 32, 64, 128, 256}.
+ * Requires H % 128 == 0, F % 128 == 0 (the kernels' column blocks are 128
+ * wide, so a multiple of 64 alone is not accepted), H <= 1048576,
+ * F <= 1048576, tile_m in {16, 32, 64, 128, 256}.
  */
 moe_status moe_grouped_ffn(const void* x_perm, const int32_t* expert_counts,
                            const int32_t* expert_offsets, const int32_t* tiles,

@@ -148,8 +148,8 @@ def test_permute_tile_sizes_with_ranks(dev, tile_m):
 
 
 def test_permute_many_tiles_with_ranks(dev):
-    # More than 4096 tiles with source ranks: the tile-list pass keeps the first 4096 tile priorities in
-    # registers across its priority passes and recomputes the rest; both must give the oracle's order.
+    # More than 4096 tiles with source ranks: each tile's place in the list comes from per-(priority,
+    # expert) tile counts over many tiles of every expert; the order must be the oracle's.
     cfg = W.MoEConfig("m", T=8300, H=64, F=128, E=64, k=8, act="swiglu", logits="normal",
                       tile_m=16, num_ranks=4)
     d = W.make_inputs(cfg, dev, weights=False)
@@ -406,7 +406,21 @@ def test_layer_full_size_sampled(dev, name):
     cfg = W.CONFIGS[name]
     d, layer, out = run_layer(cfg, dev)
     idx, w = check_layer_routing_and_permutation(cfg, d, layer)
-    toks = P.sample_tokens(cfg.T, 6, idx, cfg.expert_begin, cfg.n_local)
+    toks = set(P.sample_tokens(cfg.T, 6, idx, cfg.expert_begin, cfg.n_local))
+    if layer.tile_m >= 128:
+        # Besides the seeded sample: the tokens of the first and last real row of every row tile that
+        # the last scheduling round of either GEMM touches (split along K into partial tiles summed by
+        # a second kernel), derived from the item order on the host.
+        ref = P.oracle_permute(idx, d["src_rank"], cfg, layer.tile_m)
+        n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sched = P.ffn_schedule(len(ref["tiles"]), layer.perm.tiles_cap, cfg.H, cfg.F_loc, layer.tile_m, n_cus)
+        last = sorted(set(sched["layer0"]["last_tiles"]) | set(sched["layer1"]["last_tiles"]))
+        print(f"[schedule] {name}: {sched}", flush=True)
+        for ti in last:
+            le, r0 = ref["tiles"][ti]
+            r1 = min(r0 + layer.tile_m, ref["offsets"][le] + ref["counts"][le]) - 1
+            toks.update({int(ref["row_src"][r0]) // cfg.k, int(ref["row_src"][r1]) // cfg.k})
+    toks = sorted(toks)
     wh = P.HostWeights(d["w0"], d["w0_up"], d["w1"])
     xs = P.to_np64(d["x"][torch.tensor(toks, device=dev)])
     xfull = np.zeros((cfg.T, cfg.H))
