@@ -134,6 +134,32 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
                        int32_t* row_src, int32_t* inv_perm, int32_t* tiles,
                        int32_t* num_tiles, void* ws, size_t ws_bytes, void* stream);
 
+/* Scratch bytes moe_permute_noalloc can use: moe_permute_workspace_bytes()
+ * must not exceed this (8 MiB, e.g. T * k up to about 2 million pairs). */
+#define MOE_PERMUTE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+
+/*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments, outputs and errors as
+ * moe_permute, without ws / ws_bytes.  Its scratch is a fixed device array
+ * inside the library, one copy per GPU, held until the process ends (its
+ * address is looked up on the first call on each device); no call allocates
+ * or frees memory.  Returns MOE_ERR_WORKSPACE, launching nothing, when
+ * moe_permute_workspace_bytes(T, k, E_loc, num_ranks) exceeds
+ * MOE_PERMUTE_NOALLOC_MAX_BYTES.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and corrupt each other's
+ * results; calls ordered on one stream are safe.  Nothing in the scratch has
+ * to start at zero (each launch rewrites all it reads).
+ */
+moe_status moe_permute_noalloc(const void* x, const int32_t* topk_idx, const int32_t* src_rank,
+                               int64_t T, int32_t H, int32_t k, int32_t E, int32_t expert_begin,
+                               int32_t E_loc, int32_t num_ranks, int32_t tile_m,
+                               void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* row_src, int32_t* inv_perm, int32_t* tiles,
+                               int32_t* num_tiles, void* stream);
+
 /*
  * moe_grouped_ffn -- the experts' feed-forward networks as two grouped GEMMs
  * over all local experts (section 3.1.2: one GroupGEMM covers the experts of

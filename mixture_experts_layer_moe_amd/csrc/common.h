@@ -38,6 +38,10 @@ struct PermuteArgs {
 };
 size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Fixed per-device scratch of moe_permute_noalloc (a static device array).
+constexpr size_t kPermuteStaticWsBytes = (size_t)8 << 20;
+// Its device address on the current device (looked up on the first call per device).
+hipError_t permute_static_ws(void** ptr);
 
 struct FfnArgs {
   const uint16_t* x_perm;

@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool tile_m_ok(int32_t tm) { return tm == 16 || tm == 32 || tm == 64 || tm == 128 || tm == 256; }
@@ -56,11 +56,17 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
                                          static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* src_rank, int64_t T, int32_t H,
-                       int32_t k, int32_t E, int32_t expert_begin, int32_t E_loc, int32_t num_ranks,
-                       int32_t tile_m, void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
-                       int32_t* row_src, int32_t* inv_perm, int32_t* tiles, int32_t* num_tiles, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of moe_permute (caller's workspace) and
+// moe_permute_noalloc (static == true: the library's fixed scratch).
+moe_status permute_impl(const void* x, const int32_t* topk_idx, const int32_t* src_rank, int64_t T, int32_t H,
+                        int32_t k, int32_t E, int32_t expert_begin, int32_t E_loc, int32_t num_ranks,
+                        int32_t tile_m, void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* row_src, int32_t* inv_perm, int32_t* tiles, int32_t* num_tiles, void* ws,
+                        size_t ws_bytes, bool static_ws, void* stream) {
   if (T < 0 || H < 1 || k < 1 || E < 1 || k > E || E_loc < 1 || expert_begin < 0 ||
       (int64_t)expert_begin + E_loc > E || num_ranks < 1)
     return MOE_ERR_INVALID_ARG;
@@ -72,11 +78,18 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
   // x and x_perm both null: indices only (the rows are gathered later by moe_grouped_ffn_gather).
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
   if (x && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles, ws};
+  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (src_rank && !aligned16(src_rank)) return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < moe::permute_ws_bytes(T, k, E_loc, num_ranks)) return MOE_ERR_WORKSPACE;
+  if (static_ws) {
+    static_assert(moe::kPermuteStaticWsBytes == MOE_PERMUTE_NOALLOC_MAX_BYTES, "header and library agree");
+    if (moe::permute_ws_bytes(T, k, E_loc, num_ranks) > moe::kPermuteStaticWsBytes) return MOE_ERR_WORKSPACE;
+    if (moe::permute_static_ws(&ws) != hipSuccess) return MOE_ERR_LAUNCH;
+  } else {
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe::permute_ws_bytes(T, k, E_loc, num_ranks)) return MOE_ERR_WORKSPACE;
+  }
   moe::PermuteArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.topk_idx = topk_idx;
@@ -100,6 +113,29 @@ moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* sr
   a.num_tiles = num_tiles;
   a.ws = ws;
   return launched(moe::launch_permute(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute(const void* x, const int32_t* topk_idx, const int32_t* src_rank, int64_t T, int32_t H,
+                       int32_t k, int32_t E, int32_t expert_begin, int32_t E_loc, int32_t num_ranks,
+                       int32_t tile_m, void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* row_src, int32_t* inv_perm, int32_t* tiles, int32_t* num_tiles, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return permute_impl(x, topk_idx, src_rank, T, H, k, E, expert_begin, E_loc, num_ranks, tile_m, x_perm,
+                      expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles, ws, ws_bytes, false,
+                      stream);
+}
+
+moe_status moe_permute_noalloc(const void* x, const int32_t* topk_idx, const int32_t* src_rank, int64_t T,
+                               int32_t H, int32_t k, int32_t E, int32_t expert_begin, int32_t E_loc,
+                               int32_t num_ranks, int32_t tile_m, void* x_perm, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* row_src, int32_t* inv_perm, int32_t* tiles,
+                               int32_t* num_tiles, void* stream) {
+  return permute_impl(x, topk_idx, src_rank, T, H, k, E, expert_begin, E_loc, num_ranks, tile_m, x_perm,
+                      expert_counts, expert_offsets, row_src, inv_perm, tiles, num_tiles, nullptr, 0, true, stream);
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int32_t tile_m, int32_t H) {

@@ -35,6 +35,15 @@
 // a place launch that reads that prefix from global memory.
 #include "common.h"
 
+#include <mutex>
+
+// Scratch of moe_permute_noalloc (per-(bucket, chunk) counts and per-pair
+// ranks, as in the caller's workspace of moe_permute): a fixed device array,
+// one copy per GPU, held until the process ends.  Host code must never pass
+// its name to a kernel -- on the host it is only a stand-in symbol -- but the
+// device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[moe::kPermuteStaticWsBytes];
+
 namespace moe {
 namespace {
 
@@ -487,6 +496,26 @@ int fused_tpw(int64_t T, int64_t nb, int64_t nc) {
 }
 
 }  // namespace
+
+hipError_t permute_static_ws(void** ptr) {
+  // Device address of `scratch` on each device, looked up once with that device current.
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t permute_ws_bytes(int64_t T, int k, int E_loc, int num_ranks) {
   const int64_t nb = (int64_t)E_loc * num_ranks, nc = (T + kChunk - 1) / kChunk;

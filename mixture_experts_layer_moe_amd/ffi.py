@@ -39,6 +39,8 @@ _SIGNATURES = {
     "moe_route_topk": (ctypes.c_int, [_p, _i64, _i32, _i32, _i32, _p, _p, _p]),
     "moe_permute": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_permute_noalloc": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_ffn": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                        _i64, _i64, _p, _p, _p, _sz, _p]),
     "moe_grouped_ffn_gather": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
@@ -184,6 +186,24 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, src_rank: Optional[torc
         _ptr(out.inv_perm), _ptr(out.tiles), _ptr(out.num_tiles), _ptr(ws), ws.numel(),
         _stream(stream)))
     return out
+
+
+def moe_permute_noalloc(x: Optional[torch.Tensor], topk_idx: torch.Tensor, src_rank: Optional[torch.Tensor],
+                        H: int, E: int, expert_begin: int, E_loc: int, num_ranks: int, tile_m: int,
+                        out: Permuted, stream=None) -> int:
+    """moe_permute on the library's fixed scratch, into preallocated outputs; returns the status code.
+
+    x may be None (with out.x_perm None) for an index-only permute.  Nothing is
+    allocated here: the caller passes every output.
+    """
+    _need(topk_idx, torch.int32, "topk_idx")
+    if src_rank is not None:
+        _need(src_rank, torch.int32, "src_rank")
+    T, k = topk_idx.shape
+    return int(lib().moe_permute_noalloc(
+        _ptr(x), _ptr(topk_idx), _ptr(src_rank), T, H, k, E, expert_begin, E_loc, num_ranks, tile_m,
+        _ptr(out.x_perm), _ptr(out.expert_counts), _ptr(out.expert_offsets), _ptr(out.row_src),
+        _ptr(out.inv_perm), _ptr(out.tiles), _ptr(out.num_tiles), _stream(stream)))
 
 
 def moe_grouped_ffn(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor], w1: torch.Tensor,

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_LAUNCH"), (99, b"MOE_ERR_UNKNOWN")]:
         assert L.moe_status_str(code) == name
@@ -105,6 +105,37 @@ def test_permute_validation(L):
     need = ffi.permute_workspace_bytes(64, 2, 8, 1)
     assert permute_call(L, wsb=need - 1) == WORKSPACE
     assert permute_call(L, T=0) == OK
+
+
+def permute_noalloc_call(L, **over):
+    a = dict(x=FAKE, idx=FAKE, rank=NULL, T=64, H=512, k=2, E=8, e0=0, El=8, R=1, tm=64,
+             xp=FAKE, cnt=FAKE, off=FAKE, rs=FAKE, inv=FAKE, tiles=FAKE, nt=FAKE)
+    a.update(over)
+    return L.moe_permute_noalloc(a["x"], a["idx"], a["rank"], a["T"], a["H"], a["k"], a["E"], a["e0"], a["El"],
+                                 a["R"], a["tm"], a["xp"], a["cnt"], a["off"], a["rs"], a["inv"], a["tiles"],
+                                 a["nt"], NULL)
+
+
+def test_permute_noalloc_validation(L):
+    # Host checks only (each returns before the library looks up its scratch on a device).
+    assert permute_noalloc_call(L, e0=4, El=8) == INVALID
+    assert permute_noalloc_call(L, tm=48) == UNSUPPORTED
+    assert permute_noalloc_call(L, x=NULL) == INVALID
+    assert permute_noalloc_call(L, inv=NULL) == INVALID
+    assert permute_noalloc_call(L, T=0) == OK
+    # larger than the fixed scratch: 300000 tokens x 8 slots of per-pair ranks alone are 9.6 MB
+    limit = 8 << 20
+    assert ffi.permute_workspace_bytes(300000, 8, 8, 1) > limit >= ffi.permute_workspace_bytes(200000, 8, 8, 1)
+    assert permute_noalloc_call(L, T=300000, k=8) == WORKSPACE
+    assert ffi.permute_workspace_bytes(100000, 8, 64, 64) > limit
+    assert permute_noalloc_call(L, T=100000, k=8, El=64, E=64, R=64) == WORKSPACE   # 4096 buckets x 391 chunks
+
+
+def test_noalloc_limit_matches_header():
+    import re
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_PERMUTE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == 8 << 20
 
 
 def ffn_call(L, **over):
