@@ -173,32 +173,45 @@ def cu_partition(args):
             raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({err})")
         return h, torch.cuda.ExternalStream(h.value, device=dev)
 
-    def timed(stream_f, stream_c, reps, with_comm):
+    def once(stream_f, stream_c, with_comm):
+        """One FFN launch on stream_f, with or without the copy on stream_c: (ffn, comm, step) ms."""
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        ffn_ms, comm_ms, step_ms = [], [], []
-        for _ in range(reps):
-            torch.cuda.synchronize()
-            e[0].record(stream_f)
-            stream_c.wait_event(e[0])
-            layer.ffn(stream_f)
-            e[1].record(stream_f)
-            if with_comm:
-                with torch.cuda.stream(stream_c):
-                    staging.copy_(rows)
-                e[2].record(stream_c)
-                stream_f.wait_event(e[2])
-            e[3].record(stream_f)
-            torch.cuda.synchronize()
-            ffn_ms.append(e[0].elapsed_time(e[1]))
-            if with_comm:
-                comm_ms.append(e[0].elapsed_time(e[2]))
-            step_ms.append(e[0].elapsed_time(e[3]))
-        med = lambda v: sorted(v)[len(v) // 2] if v else None
-        return med(ffn_ms), med(comm_ms), med(step_ms)
+        torch.cuda.synchronize()
+        e[0].record(stream_f)
+        stream_c.wait_event(e[0])
+        layer.ffn(stream_f)
+        e[1].record(stream_f)
+        if with_comm:
+            with torch.cuda.stream(stream_c):
+                staging.copy_(rows)
+            e[2].record(stream_c)
+            stream_f.wait_event(e[2])
+        e[3].record(stream_f)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]), e[0].elapsed_time(e[2]) if with_comm else None, e[0].elapsed_time(e[3])
 
-    reps = max(3, min(args.steps, 20))
+    med = lambda v: sorted(v)[len(v) // 2]
+
+    def paired(stream_f, stream_c, reps):
+        """The FFN alone and with the copy, alternating rep by rep after two warm-up pairs, so that
+        clock and cache drift fall on both alike: medians of (alone ffn, ffn, comm, step)."""
+        for _ in range(2):
+            once(stream_f, stream_c, False)
+            once(stream_f, stream_c, True)
+        a, f, c, st = [], [], [], []
+        for _ in range(reps):
+            a.append(once(stream_f, stream_c, False)[0])
+            r = once(stream_f, stream_c, True)
+            f.append(r[0])
+            c.append(r[1])
+            st.append(r[2])
+        return med(a), med(f), med(c), med(st)
+
+    reps = max(5, min(args.steps, 20))
     base = torch.cuda.current_stream()
-    full_ffn, _, _ = timed(base, base, reps, False)
+    for _ in range(2):
+        once(base, base, False)
+    full_ffn = med([once(base, base, False)[0] for _ in range(reps)])
     curve = []
     per_xcd = n // 8
     for nc in (per_xcd, 2 * per_xcd, 3 * per_xcd, 4 * per_xcd):
@@ -206,8 +219,7 @@ def cu_partition(args):
             break
         hc, sc = masked_stream(range(nc))
         hf, sf = masked_stream(range(nc, n))
-        alone, _, _ = timed(sf, sc, reps, False)
-        ffn, comm, step = timed(sf, sc, reps, True)
+        alone, ffn, comm, step = paired(sf, sc, reps)
         torch.cuda.synchronize()
         hip.hipStreamDestroy(hc)
         hip.hipStreamDestroy(hf)
