@@ -395,13 +395,14 @@ def main():
     layer = MoELayer.from_inputs(cfg, d)
     stream = torch.cuda.current_stream()
 
-    names = ["route", "permute", "grouped_ffn", "combine"]
-
     def timed_steps(lay):
         """W warm-up steps, then K timed steps: (ms per step, per-call ms)."""
         for _ in range(args.warmup):
             lay.run()
-        calls = [lay.route, lay.permute, lay.ffn, lay.combine]
+        if lay.signalled:
+            calls, names = [lay.route, lay.permute, lay.ffn_combine], ["route", "permute", "ffn_combine"]
+        else:
+            calls, names = [lay.route, lay.permute, lay.ffn, lay.combine], ["route", "permute", "grouped_ffn", "combine"]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -465,6 +466,14 @@ def main():
     result["fused_gather"] = {"ms_per_step": round(g_ms, 5), "value": round(flop / (g_ms * 1e-3) / 1e12, 3),
                               "per_call_ms": {n: round(v, 5) for n, v in g_calls.items()}}
     del gl
+    # The grouped FFN and the combine as one launch with tile-level signals (moe_ffn_combine_fused,
+    # 256-row tiles only), also after the main line on its own buffers.
+    if layer.tile_m == 256:
+        sl = MoELayer.from_inputs(cfg, d, signalled=True)
+        s_ms, s_calls = timed_steps(sl)
+        result["signalled"] = {"ms_per_step": round(s_ms, 5), "value": round(flop / (s_ms * 1e-3) / 1e12, 3),
+                               "per_call_ms": {n: round(v, 5) for n, v in s_calls.items()}}
+        del sl
     copy_gbps, cold = copy_and_cold(layer, stream)
     result["copy_GBps"] = round(copy_gbps, 1)
     result["permute_GBps_cold"] = round(permute_bytes / (cold["permute"] * 1e-3) / 1e9, 1)

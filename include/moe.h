@@ -226,6 +226,46 @@ moe_status moe_grouped_ffn_gather(const void* x, const int32_t* row_src, int64_t
                                   int64_t tiles_cap, void* act_buf, float* y_perm, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace moe_ffn_combine_fused needs for this tile capacity
+ * and H on the current device (0 on invalid arguments or H % 256 != 0). */
+size_t moe_ffn_combine_fused_workspace_bytes(int64_t tiles_cap, int32_t H);
+
+/*
+ * moe_ffn_combine_fused -- moe_grouped_ffn followed by moe_combine as one
+ * persistent launch with tile-level signals (section 3.1.2: layer1's reduce
+ * and its hand-off can begin once the first column blocks are done;
+ * tile-level-signalling follow-up, abstract: tiles are signalled to their
+ * consumers as they become ready instead of at kernel boundaries).  Every
+ * workgroup takes work items in one global order -- layer0 tiles, layer1
+ * tiles column group by column group, the K slices of the last layer1 items,
+ * then combine blocks of 64 tokens per column group -- and a layer1 item
+ * starts as soon as the layer0 items of its row tile have signalled, a
+ * combine block as soon as its column group's layer1 items have.
+ *
+ * Arguments, layouts and results are those of moe_grouped_ffn (act_buf,
+ * y_perm) and moe_combine (inv_perm, topk_w, T, k, out): act_buf, y_perm and
+ * out equal what the two calls give, up to fp32 summation order in layer1's
+ * split items (deterministic run to run).  Requires tile_m == 256,
+ * H % 256 == 0, F % 128 == 0, k <= 32.
+ * ws / ws_bytes: device workspace of at least
+ * moe_ffn_combine_fused_workspace_bytes(tiles_cap, H), ZERO-FILLED before its
+ * first use; every launch leaves its counters zero again for the next one (so
+ * no clearing is needed between calls, including replays of a captured
+ * graph).  Its first int32 is an error word: nonzero after a launch means a
+ * wait between work items timed out and that launch's outputs are invalid
+ * (the launch still ends); the caller reads it after synchronising and
+ * writes it back to zero.  One workspace must not be used by two launches
+ * that may overlap.
+ */
+moe_status moe_ffn_combine_fused(const void* x_perm, const int32_t* expert_counts,
+                                 const int32_t* expert_offsets, const int32_t* tiles,
+                                 const int32_t* num_tiles, const void* w0, const void* w0_up,
+                                 const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act,
+                                 int32_t tile_m, int64_t R_cap, int64_t tiles_cap, void* act_buf,
+                                 float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                                 int64_t T, int32_t k, float* out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /*
  * moe_combine -- gather and top-k reduce (section 2.1: expert outputs are
  * gathered back to their tokens and reduced over the top-k choices).

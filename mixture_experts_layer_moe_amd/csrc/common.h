@@ -62,6 +62,9 @@ struct FfnArgs {
 };
 size_t grouped_ffn_ws_bytes(int tile_m, int H);
 hipError_t launch_grouped_ffn(const FfnArgs& a);
+// One persistent launch of layer0, layer1 and the combine with tile-level signals (tile_m 256).
+size_t fused_ffn_ws_bytes(int64_t tiles_cap, int H);
+hipError_t launch_ffn_fused(const FfnArgs& a, const int32_t* inv_perm, const float* topk_w, float* out);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                           int64_t T, int k, int H, int64_t R_cap, float* out, hipStream_t s);

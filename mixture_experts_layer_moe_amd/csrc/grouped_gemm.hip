@@ -176,11 +176,23 @@ __device__ __forceinline__ void item_coords(int64_t item, int nt, int nbn, int& 
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) { return (bid % kXcds) * (G / kXcds) + bid / kXcds; }
 
-// Epilogue for 4 consecutive output columns of one row.
-template <int EPI>
+// 8 bytes stored for device-scope visibility: an agent-scope relaxed atomic store, which the
+// compiler emits as a store that writes through this XCD's L2 (sc1), so a workgroup on another XCD that
+// reads the line after the producer's counter increment finds it in memory (its own L2 never held it).
+__device__ __forceinline__ void store8_coh(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Epilogue for 4 consecutive output columns of one row.  COH: the stores are visible device-wide once
+// they have completed (for a consumer in the same launch, see store8_coh).
+template <int EPI, bool COH = false>
 __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const float* g, const float* u) {
   static_assert(EPI != EPI_PARTIAL, "partial tiles are stored as two fp32 halves");
-  if (EPI == EPI_F32) {
+  if (EPI == EPI_F32 && COH) {
+    float* d = static_cast<float*>(C) + row * N + n;
+    store8_coh(d, (uint64_t)__builtin_bit_cast(uint32_t, g[0]) | ((uint64_t)__builtin_bit_cast(uint32_t, g[1]) << 32));
+    store8_coh(d + 2, (uint64_t)__builtin_bit_cast(uint32_t, g[2]) | ((uint64_t)__builtin_bit_cast(uint32_t, g[3]) << 32));
+  } else if (EPI == EPI_F32) {
     *reinterpret_cast<floatx4*>(static_cast<float*>(C) + row * N + n) = floatx4{g[0], g[1], g[2], g[3]};
   } else {
     uint16_t h[4];
@@ -190,7 +202,10 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
       h[q] = f2bf_bits(a);
     }
     const uint2 packed = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) = packed;
+    if (COH)
+      store8_coh(static_cast<uint16_t*>(C) + row * N + n, (uint64_t)packed.x | ((uint64_t)packed.y << 32));
+    else
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) = packed;
   }
 }
 
@@ -212,7 +227,7 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 // GATHER: A is the token matrix x [T, K] itself and padded row p of the tile
 // reads token row_src[p] / topk (row_src < 0: padding, read as zeros) -- the
 // layer0 operand gathered on the fly instead of from a permuted copy.
-template <int BM, int BN, bool DUAL, int EPI, int STAGES, bool GATHER>
+template <int BM, int BN, bool DUAL, int EPI, int STAGES, bool GATHER, bool COH = false>
 __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
                                           int N, int K, int le, int row0, int valid, int n0, int k_begin, int k_len,
@@ -554,10 +569,10 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
           u[r] = acc[NMAT - 1][j][i][q * 4 + r];
         }
         if constexpr (EPI == EPI_PARTIAL) {
-          store4<EPI_F32>(C, row, ldc, n, g, g);
-          if (NMAT == 2) store4<EPI_F32>(C, row, ldc, n + BN, u, u);
+          store4<EPI_F32, COH>(C, row, ldc, n, g, g);
+          if (NMAT == 2) store4<EPI_F32, COH>(C, row, ldc, n + BN, u, u);
         } else {
-          store4<EPI>(C, row, ldc, n, g, u);
+          store4<EPI, COH>(C, row, ldc, n, g, u);
         }
       }
   }
@@ -697,6 +712,240 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
     }
     const float g[4] = {g4[0], g4[1], g4[2], g4[3]}, uu[4] = {u4[0], u4[1], u4[2], u4[3]};
     store4<EPI>(C, (int64_t)row0 + m, N, nb * BN + c4 * 4, g, uu);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One persistent launch for layer0 -> activation -> layer1 -> top-k combine, with tile-level signals.
+//
+// Comet section 3.1.2: layer1's N-decomposed reduction can start after its first column blocks;
+// tile-level-signalling follow-up (abstract): tiles are signalled as they become ready instead of
+// waiting for whole kernels.  Here every workgroup takes work items in one global order from a device
+// counter: all layer0 items (256-row tile x 128 columns of F, the unfused order), then layer1 items
+// (tile x 256 columns of H, column groups of kGroupN blocks first), then the K slices of the last
+// layer1 items (as many as the unfused layer1 would leave for its last round), then combine items
+// (64 tokens x one column group, group by group).  Signals:
+//   ready[tile]   layer0 items of the tile done; a layer1 item waits for F / 128 of them;
+//   group[g]      layer1 items (a split item counting once, when its last slice has reduced) of column
+//                 group g done; a combine item waits for num_tiles x (blocks of g) of them;
+//   slices[u]     K slices of split item u done; the one that brings it to S sums all S in slice order.
+// A workgroup only ever waits for items that come before its own in the global order, all of them
+// taken by workgroups that are running, so every wait ends; each is still bounded (on time-out the
+// error word is set and the item proceeds, giving wrong values rather than a hang).
+// Visibility across XCDs without an L2 write-back: every result another workgroup reads (activations,
+// layer1 rows, partial slices) is stored with device-scope stores that write through L2; the producer
+// waits for its stores, synchronises its workgroup and then increments the counter; the consumer polls
+// with device-scope loads and then reads the data, which its own L2 and L1 have not held since the
+// launch began (each row range is produced once and read only after its signal).  The last workgroup to
+// finish returns every counter it used to zero for the next launch.
+// ---------------------------------------------------------------------------
+constexpr int kCombineTokens = 64;
+constexpr int kCombineLoads = 16;   // y rows in flight per thread in a combine item
+constexpr int kMaxTopk = 32;      // the entry point's limit on k
+constexpr int64_t kSpinLimit = 1 << 20;
+
+struct FusedCounters {
+  int err;            // nonzero: a wait timed out (the launch's results are not valid); cleared by the caller
+  int done;           // workgroups finished
+  int pad[2];
+  int next[kXcds];    // next work item of each XCD's queue
+};
+
+// Thread 0: poll *p (device-scope loads) until it reaches target; false (and the error word set) on time-out.
+__device__ __forceinline__ bool wait_count(int* p, int target, int* err) {
+  for (int64_t it = 0;; ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+    if (it >= kSpinLimit) {
+      __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// After the workgroup's device-scope stores: every wave waits for its own, then thread 0 signals.
+__device__ __forceinline__ int publish(int* p) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  int old = 0;
+  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
+
+template <bool DUAL, int EPI0>
+__global__ __launch_bounds__(256, 1) void ffn_fused_kernel(
+    const uint16_t* __restrict__ x_perm, const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w0_up,
+    const uint16_t* __restrict__ w1, int H, int F, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+    int64_t tiles_cap, int64_t R_cap, int E_loc, uint16_t* __restrict__ act, float* __restrict__ y,
+    const int32_t* __restrict__ inv_perm, const float* __restrict__ topk_w, int64_t T, int topk,
+    float* __restrict__ out, FusedCounters* __restrict__ ctr, int* __restrict__ ready, int* __restrict__ group,
+    int* __restrict__ slices, float* __restrict__ part) {
+  constexpr int BM = 256, BN0 = 128, BN1 = 256;
+  __shared__ __attribute__((aligned(1024))) char smem[big_lds_bytes<BM, BN1, false>(2)];
+  static_assert(big_lds_bytes<BM, BN0, DUAL>(2) <= big_lds_bytes<BM, BN1, false>(2), "layer0 stages fit");
+  __shared__ int s_item, s_flag;
+  __shared__ int s_row[kCombineTokens * kMaxTopk];
+  __shared__ float s_w[kCombineTokens * kMaxTopk];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x;
+  int nt = *num_tiles;
+  if (nt > tiles_cap) nt = (int)tiles_cap;
+  const int nb0 = F / BN0, nb1 = H / BN1;
+  const int ngroups = (nb1 + kGroupN - 1) / kGroupN;
+  const int64_t W0 = (int64_t)nt * nb0, W1 = (int64_t)nt * nb1;
+  const int64_t R1 = W1 % G;                                  // items the unfused layer1 leaves for its last round
+  const int S = R1 > 0 ? tail_ksplit(R1, G, F / BK) : 1;
+  const int64_t W1w = S > 1 ? W1 - R1 : W1;                   // layer1 items run whole
+  const int64_t P1 = S > 1 ? R1 * S : 0;                      // their K slices
+  const int64_t TC = (T + kCombineTokens - 1) / kCombineTokens;
+  const int64_t total = W0 + W1w + P1 + TC * ngroups;
+
+  auto tile_of = [&](int tile_i, int& le, int& row0, int& valid) {
+    le = tiles[2 * tile_i];
+    row0 = tiles[2 * tile_i + 1];
+    if (le < 0 || le >= E_loc || row0 < 0 || (int64_t)row0 + BM > R_cap) return false;
+    valid = counts[le] - (row0 - offsets[le]);
+    valid = valid < BM ? valid : BM;
+    return true;
+  };
+  // Layer1 item u's tile, column block and column group; waits for the tile's activations.
+  auto layer1_coords = [&](int64_t u, int& tile_i, int& nb) {
+    item_coords<ORDER_N>(u, nt, nb1, tile_i, nb);
+    if (threadIdx.x == 0) wait_count(&ready[tile_i], nb0, &ctr->err);
+    __syncthreads();
+  };
+
+  // Each XCD (workgroups b with b % 8 == x, dispatched round-robin over the XCDs) has its own queue: its
+  // k-th item is item (k / C) * G + x * C + k % C (C = G / 8), so in every round of G items it runs a
+  // contiguous run of C of them, the rectangle of row tiles x column blocks that shares operand panels
+  // in its L2 (the unfused kernels' item placement), and each queue runs in increasing item order.
+  const int xq = blockIdx.x % kXcds, C = G / kXcds;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(&ctr->next[xq], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t kq = s_item;
+    const int64_t item = kq / C * G + (int64_t)xq * C + kq % C;
+    __syncthreads();
+    if (item >= total) break;
+    if (item < W0) {  // layer0: activations of a tile's 128 columns
+      int tile_i, nb, le, row0, valid;
+      item_coords<ORDER_M>(item, nt, nb0, tile_i, nb);
+      if (tile_of(tile_i, le, row0, valid))
+        gemm_item<BM, BN0, DUAL, EPI0, 2, false, true>(smem, x_perm, w0, w0_up, F, H, le, row0, valid, nb * BN0, 0, H,
+                                                      act, row0, F, nb * BN0, wave, lane, nullptr, 0, 0);
+      publish(&ready[tile_i]);
+    } else if (item < W0 + W1w) {  // layer1, whole item
+      int tile_i, nb, le, row0, valid;
+      layer1_coords(item - W0, tile_i, nb);
+      if (tile_of(tile_i, le, row0, valid))
+        gemm_item<BM, BN1, false, EPI_F32, 2, false, true>(smem, act, w1, nullptr, H, F, le, row0, valid, nb * BN1, 0,
+                                                          F, y, row0, H, nb * BN1, wave, lane, nullptr, 0, 0);
+      publish(&group[nb / kGroupN]);
+    } else if (item < W0 + W1w + P1) {  // layer1, one K slice of a split item
+      const int64_t pc = item - W0 - W1w, u = pc / S;
+      const int s = (int)(pc % S), nk = F / BK, kb = s * nk / S, ke = (s + 1) * nk / S;
+      int tile_i, nb, le, row0, valid;
+      layer1_coords(W1w + u, tile_i, nb);
+      const bool ok = tile_of(tile_i, le, row0, valid);
+      if (ok)
+        gemm_item<BM, BN1, false, EPI_PARTIAL, 2, false, true>(smem, act, w1, nullptr, H, F, le, row0, valid,
+                                                              nb * BN1, kb * BK, (ke - kb) * BK,
+                                                              part + pc * (int64_t)(BM * BN1), 0, BN1, 0, wave, lane,
+                                                              nullptr, 0, 0);
+      const int old = publish(&slices[u]);
+      if (threadIdx.x == 0) s_flag = old;
+      __syncthreads();
+      if (s_flag == S - 1) {  // the last slice of item u: sum the S slices in order, store the rows, signal
+        if (ok) {
+          const float* base = part + u * S * (int64_t)(BM * BN1);
+          for (int e = threadIdx.x; e < valid * (BN1 / 4); e += 256) {
+            const int m = e / (BN1 / 4), c4 = e % (BN1 / 4);
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < S; ++q) {
+              const float* src = base + q * (int64_t)(BM * BN1) + m * BN1 + c4 * 4;
+              const uint64_t lo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+              const uint64_t hi = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src + 2), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+              acc += floatx4{__builtin_bit_cast(float, (uint32_t)lo), __builtin_bit_cast(float, (uint32_t)(lo >> 32)),
+                             __builtin_bit_cast(float, (uint32_t)hi), __builtin_bit_cast(float, (uint32_t)(hi >> 32))};
+            }
+            const float g[4] = {acc[0], acc[1], acc[2], acc[3]};
+            store4<EPI_F32, true>(y, (int64_t)row0 + m, H, nb * BN1 + c4 * 4, g, g);
+          }
+        }
+        publish(&group[nb / kGroupN]);
+      }
+    } else {  // combine: kCombineTokens tokens x one column group
+      const int64_t c = item - W0 - W1w - P1;
+      const int g = (int)(c / TC);
+      const int64_t t0 = (c % TC) * kCombineTokens;
+      const int nt_c = (int)(T - t0 < kCombineTokens ? T - t0 : kCombineTokens);
+      const int gsize = (nb1 - g * kGroupN) < kGroupN ? (nb1 - g * kGroupN) : kGroupN;
+      // The item's routing slots (row, weight) into LDS while the group's layer1 items finish.
+      for (int e = threadIdx.x; e < nt_c * topk; e += 256) {
+        const int p = inv_perm[t0 * topk + e];
+        s_row[e] = (p < 0 || p >= R_cap) ? -1 : p;
+        s_w[e] = topk_w[t0 * topk + e];
+      }
+      if (threadIdx.x == 0) wait_count(&group[g], nt * gsize, &ctr->err);
+      __syncthreads();
+      const int col = g * kGroupN * BN1 + threadIdx.x * 4;  // this thread's float4 column of the group
+      if (threadIdx.x * 4 < gsize * BN1) {
+        // Up to kCombineLoads rows in flight per thread: U whole tokens at a time (topk above the window:
+        // one token, its first kCombineLoads rows in flight), each token summed in slot order.
+        const int U = topk >= kCombineLoads ? 1 : kCombineLoads / topk;
+        for (int tb = 0; tb < nt_c; tb += U) {
+          const int ue = nt_c - tb < U ? nt_c - tb : U;
+          const int nq = ue * topk;
+          const int* rows = s_row + tb * topk;
+          const float* ws = s_w + tb * topk;
+          floatx4 v[kCombineLoads];
+#pragma unroll
+          for (int q = 0; q < kCombineLoads; ++q) {
+            const int p = q < nq ? rows[q] : -1;
+            v[q] = p >= 0 ? *reinterpret_cast<const floatx4*>(y + (int64_t)p * H + col) : floatx4{0.f, 0.f, 0.f, 0.f};
+          }
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          int j = 0;
+          float* o = out + (t0 + tb) * H + col;
+#pragma unroll
+          for (int q = 0; q < kCombineLoads; ++q) {
+            if (q < nq) {
+              acc += ws[q] * v[q];
+              if (++j == topk) {
+                *reinterpret_cast<floatx4*>(o) = acc;
+                acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                j = 0;
+                o += H;
+              }
+            }
+          }
+          if (topk > kCombineLoads) {
+            for (int q = kCombineLoads; q < topk; ++q) {
+              const int p = rows[q];
+              if (p >= 0) acc += ws[q] * *reinterpret_cast<const floatx4*>(y + (int64_t)p * H + col);
+            }
+            *reinterpret_cast<floatx4*>(o) = acc;
+          }
+        }
+      }
+      __syncthreads();  // s_row / s_w are rewritten by the next combine item
+    }
+  }
+  // The last workgroup to finish resets the counters of this launch for the next one.
+  if (threadIdx.x == 0) {
+    const int d = __hip_atomic_fetch_add(&ctr->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = d;
+  }
+  __syncthreads();
+  if (s_flag == G - 1) {
+    for (int64_t i = threadIdx.x; i < nt; i += 256) ready[i] = 0;
+    for (int i = threadIdx.x; i < ngroups; i += 256) group[i] = 0;
+    for (int64_t i = threadIdx.x; i < R1; i += 256) slices[i] = 0;
+    if (threadIdx.x < kXcds) ctr->next[threadIdx.x] = 0;
+    if (threadIdx.x == 0) ctr->done = 0;
   }
 }
 
@@ -981,7 +1230,51 @@ hipError_t launch_small(const FfnArgs& a) {
                            a.tiles_cap * (a.H / BN1), a.act_buf, a.w1, nullptr, a.H, a.F, a, a.y_perm, (const int32_t*)nullptr, 0, (int64_t)0);
 }
 
+// Workspace of the fused launch: counters (zero before the first launch; every launch leaves them zero),
+// then the K-slice partial tiles of the split layer1 items.
+struct FusedWs {
+  FusedCounters* ctr;
+  int *ready, *group, *slices;
+  float* part;
+};
+__host__ __device__ inline int64_t fused_ints(int64_t tiles_cap, int H, int G) {
+  return (int64_t)(sizeof(FusedCounters) / 4) + tiles_cap + (H / 256 + kGroupN - 1) / kGroupN + G;
+}
+inline FusedWs fused_ws(void* ws, int64_t tiles_cap, int H, int G) {
+  FusedWs w;
+  char* p = static_cast<char*>(ws);
+  w.ctr = reinterpret_cast<FusedCounters*>(p);
+  w.ready = reinterpret_cast<int*>(p) + sizeof(FusedCounters) / 4;
+  w.group = w.ready + tiles_cap;
+  w.slices = w.group + (H / 256 + kGroupN - 1) / kGroupN;
+  w.part = reinterpret_cast<float*>(p + (fused_ints(tiles_cap, H, G) * 4 + 255) / 256 * 256);
+  return w;
+}
+
 }  // namespace
+
+size_t fused_ffn_ws_bytes(int64_t tiles_cap, int H) {
+  const int G = (int)persistent_grid(INT32_MAX, num_cus());
+  return (size_t)((fused_ints(tiles_cap, H, G) * 4 + 255) / 256 * 256) + (size_t)G * 256 * 256 * sizeof(float);
+}
+
+hipError_t launch_ffn_fused(const FfnArgs& args, const int32_t* inv_perm, const float* topk_w, float* out) {
+  FfnArgs a = args;
+  a.cus = stream_cus(a.stream);
+  const int G = (int)persistent_grid(INT32_MAX, a.cus);
+  const FusedWs w = fused_ws(a.ws, a.tiles_cap, a.H, (int)persistent_grid(INT32_MAX, num_cus()));
+  if (a.act == MOE_ACT_SWIGLU_I)
+    hipLaunchKernelGGL((ffn_fused_kernel<true, EPI_SWIGLU>), dim3(G), dim3(256), 0, a.stream, a.x_perm, a.w0, a.w0_up,
+                       a.w1, a.H, a.F, a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc,
+                       a.act_buf, a.y_perm, inv_perm, topk_w, a.T, a.topk, out, w.ctr, w.ready, w.group, w.slices,
+                       w.part);
+  else
+    hipLaunchKernelGGL((ffn_fused_kernel<false, EPI_GELU>), dim3(G), dim3(256), 0, a.stream, a.x_perm, a.w0, nullptr,
+                       a.w1, a.H, a.F, a.counts, a.offsets, a.tiles, a.num_tiles, a.tiles_cap, a.R_cap, a.E_loc,
+                       a.act_buf, a.y_perm, inv_perm, topk_w, a.T, a.topk, out, w.ctr, w.ready, w.group, w.slices,
+                       w.part);
+  return hipGetLastError();
+}
 
 size_t grouped_ffn_ws_bytes(int tile_m, int H) {
   // Split-K partial tiles of either layer's last round: at most one round of

@@ -5,7 +5,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool tile_m_ok(int32_t tm) { return tm == 16 || tm == 32 || tm == 64 || tm == 128 || tm == 256; }
@@ -222,6 +222,55 @@ moe_status moe_grouped_ffn_gather(const void* x, const int32_t* row_src, int64_t
   if (!x) return MOE_ERR_INVALID_ARG;
   return grouped_ffn_impl(nullptr, x, row_src, T, k, expert_counts, expert_offsets, tiles, num_tiles, w0, w0_up, w1,
                           E_loc, H, F, act, tile_m, R_cap, tiles_cap, act_buf, y_perm, ws, ws_bytes, stream);
+}
+
+size_t moe_ffn_combine_fused_workspace_bytes(int64_t tiles_cap, int32_t H) {
+  if (tiles_cap < 0 || H < 256 || H % 256 != 0 || tiles_cap > INT32_MAX / 2) return 0;
+  return moe::fused_ffn_ws_bytes(tiles_cap, H);
+}
+
+moe_status moe_ffn_combine_fused(const void* x_perm, const int32_t* expert_counts, const int32_t* expert_offsets,
+                                 const int32_t* tiles, const int32_t* num_tiles, const void* w0, const void* w0_up,
+                                 const void* w1, int32_t E_loc, int32_t H, int32_t F, int32_t act, int32_t tile_m,
+                                 int64_t R_cap, int64_t tiles_cap, void* act_buf, float* y_perm,
+                                 const int32_t* inv_perm, const float* topk_w, int64_t T, int32_t k, float* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (E_loc < 1 || H < 1 || F < 1 || R_cap < 0 || tiles_cap < 0 || T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (act != MOE_ACT_GELU && act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if ((act == MOE_ACT_SWIGLU) != (w0_up != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (tile_m != 256 || H % 256 != 0 || F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H > (1 << 20) || F > (1 << 20) || k > 32) return MOE_ERR_UNSUPPORTED;
+  if (R_cap > INT32_MAX || tiles_cap > INT32_MAX / 2 || T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const void* ptrs[] = {x_perm, expert_counts, expert_offsets, tiles, num_tiles, w0, w1, act_buf, y_perm,
+                        inv_perm, topk_w, out, ws};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (w0_up && !aligned16(w0_up)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::fused_ffn_ws_bytes(tiles_cap, H)) return MOE_ERR_WORKSPACE;
+  moe::FfnArgs a{};
+  a.x_perm = static_cast<const uint16_t*>(x_perm);
+  a.counts = expert_counts;
+  a.offsets = expert_offsets;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.w0 = static_cast<const uint16_t*>(w0);
+  a.w0_up = static_cast<const uint16_t*>(w0_up);
+  a.w1 = static_cast<const uint16_t*>(w1);
+  a.E_loc = E_loc;
+  a.H = H;
+  a.F = F;
+  a.act = act;
+  a.tile_m = tile_m;
+  a.R_cap = R_cap;
+  a.tiles_cap = tiles_cap;
+  a.act_buf = static_cast<uint16_t*>(act_buf);
+  a.y_perm = y_perm;
+  a.ws = ws;
+  a.topk = k;
+  a.T = T;
+  a.stream = static_cast<hipStream_t>(stream);
+  return launched(moe::launch_ffn_fused(a, inv_perm, topk_w, out));
 }
 
 moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w, int64_t T, int32_t k,

@@ -45,6 +45,9 @@ _SIGNATURES = {
                                        _i64, _i64, _p, _p, _p, _sz, _p]),
     "moe_grouped_ffn_gather": (ctypes.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
                                               _i32, _i32, _i64, _i64, _p, _p, _p, _sz, _p]),
+    "moe_ffn_combine_fused_workspace_bytes": (_sz, [_i64, _i32]),
+    "moe_ffn_combine_fused": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                             _p, _p, _p, _p, _i64, _i32, _p, _p, _sz, _p]),
     "moe_combine": (ctypes.c_int, [_p, _p, _p, _i64, _i32, _i32, _i64, _p, _p]),
 }
 
@@ -256,6 +259,50 @@ def moe_grouped_ffn_gather(x: torch.Tensor, p: Permuted, w0: torch.Tensor, w0_up
         p.tiles_cap, _ptr(act_buf), _ptr(y_perm), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream(stream)))
     return act_buf, y_perm
+
+
+def fused_workspace_bytes(tiles_cap: int, H: int) -> int:
+    return int(lib().moe_ffn_combine_fused_workspace_bytes(tiles_cap, H))
+
+
+def alloc_fused_workspace(tiles_cap: int, H: int, device) -> torch.Tensor:
+    """Zero-filled workspace of moe_ffn_combine_fused (each launch leaves it zero again)."""
+    nbytes = fused_workspace_bytes(tiles_cap, H)
+    if nbytes == 0:
+        raise ValueError("moe_ffn_combine_fused does not support this shape")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def fused_error_word(ws: torch.Tensor) -> int:
+    """The fused launch's error word (nonzero: a wait timed out; the caller clears it)."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def moe_ffn_combine_fused(p: Permuted, w0: torch.Tensor, w0_up: Optional[torch.Tensor], w1: torch.Tensor,
+                          act: str, topk_w: torch.Tensor, ws: torch.Tensor,
+                          act_buf: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, stream=None):
+    """Grouped FFN and combine as one launch with tile-level signals; returns (act_buf, y_perm, out)."""
+    _need(w0, torch.bfloat16, "w0")
+    _need(w1, torch.bfloat16, "w1")
+    _need(topk_w, torch.float32, "topk_w")
+    if w0_up is not None:
+        _need(w0_up, torch.bfloat16, "w0_up")
+    E_loc, F, H = w0.shape
+    T, k = p.inv_perm.shape
+    dev = w0.device
+    if act_buf is None:
+        act_buf = torch.empty((p.R_cap, F), dtype=torch.bfloat16, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty((p.R_cap, H), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _check("moe_ffn_combine_fused", lib().moe_ffn_combine_fused(
+        _ptr(p.x_perm), _ptr(p.expert_counts), _ptr(p.expert_offsets), _ptr(p.tiles), _ptr(p.num_tiles),
+        _ptr(w0), _ptr(w0_up), _ptr(w1), E_loc, H, F, ACTS[act], p.tile_m, p.R_cap, p.tiles_cap,
+        _ptr(act_buf), _ptr(y_perm), _ptr(p.inv_perm), _ptr(topk_w), T, k, _ptr(out), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return act_buf, y_perm, out
 
 
 def moe_combine(y_perm: torch.Tensor, inv_perm: torch.Tensor, topk_w: torch.Tensor,

@@ -5,7 +5,9 @@ moe_route_topk -> moe_permute -> moe_grouped_ffn -> moe_combine on one stream
 with no host synchronisation in between (every data-dependent size stays on
 the device), so the whole layer can also be captured in a HIP graph.  With
 fused_gather=True the permute writes indices only and moe_grouped_ffn_gather
-reads layer0's token rows straight from x (no x_perm).
+reads layer0's token rows straight from x (no x_perm).  With signalled=True
+the grouped FFN and the combine run as one launch with tile-level signals
+(moe_ffn_combine_fused; 256-row tiles).
 """
 from __future__ import annotations
 
@@ -21,9 +23,10 @@ class MoELayer:
     def __init__(self, cfg: MoEConfig, x: torch.Tensor, logits: torch.Tensor,
                  src_rank: Optional[torch.Tensor], w0: torch.Tensor, w0_up: Optional[torch.Tensor],
                  w1: torch.Tensor, tile_m: Optional[int] = None, renormalize: bool = True,
-                 fused_gather: bool = False):
+                 fused_gather: bool = False, signalled: bool = False):
         self.cfg = cfg
         self.fused_gather = fused_gather
+        self.signalled = signalled
         self.tile_m = tile_m or cfg.tile_m
         self.renormalize = renormalize
         self.x, self.logits, self.src_rank = x, logits, src_rank
@@ -40,6 +43,7 @@ class MoELayer:
         ffn_bytes = ffi.grouped_ffn_workspace_bytes(self.tile_m, H)
         self.ffn_ws = torch.empty(ffn_bytes, dtype=torch.uint8, device=dev) if ffn_bytes else None
         self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.fused_ws = ffi.alloc_fused_workspace(self.perm.tiles_cap, H, dev) if signalled else None
 
     @classmethod
     def from_inputs(cls, cfg: MoEConfig, inputs: dict, **kw) -> "MoELayer":
@@ -66,9 +70,17 @@ class MoELayer:
     def combine(self, stream=None):
         ffi.moe_combine(self.y_perm, self.perm.inv_perm, self.topk_w, self.out, stream)
 
+    def ffn_combine(self, stream=None):
+        """The grouped FFN and the combine as one launch with tile-level signals."""
+        ffi.moe_ffn_combine_fused(self.perm, self.w0, self.w0_up, self.w1, self.cfg.act, self.topk_w,
+                                  self.fused_ws, self.act_buf, self.y_perm, self.out, stream)
+
     def run(self, stream=None) -> torch.Tensor:
         self.route(stream)
         self.permute(stream)
-        self.ffn(stream)
-        self.combine(stream)
+        if self.signalled:
+            self.ffn_combine(stream)
+        else:
+            self.ffn(stream)
+            self.combine(stream)
         return self.out

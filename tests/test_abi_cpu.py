@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
                        (3, b"MOE_ERR_WORKSPACE"), (4, b"MOE_ERR_LAUNCH"), (99, b"MOE_ERR_UNKNOWN")]:
         assert L.moe_status_str(code) == name

@@ -1,0 +1,143 @@
+"""moe_ffn_combine_fused: the grouped FFN and the combine as one launch with tile-level signals.
+
+Comet (section 3.1.2) lets layer1's reduce start once its first column blocks
+are done; the tile-level-signalling follow-up (abstract) signals tiles to
+their consumers as they become ready.  The fused launch must give the layer
+the oracle gives, on its own and against the two-call path, stay bitwise
+reproducible, leave its counters ready for the next launch (including graph
+replays) and never report a timed-out wait.  Small layers are checked in full
+(on the whole device and on a one-XCD stream, where layer1 has more items
+than workgroups and its last items are split along K); full-size layers on
+sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_moe_amd import ffi
+from mixture_experts_layer_moe_amd import workloads as W
+from mixture_experts_layer_moe_amd.layer import MoELayer
+from oracle import moe_oracle as O
+
+import parity_helpers as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = P.require_gpu()
+    ffi.lib()
+    return d
+
+
+def run_fused(cfg, d, stream=None):
+    layer = MoELayer.from_inputs(cfg, d, signalled=True)
+    layer.act_buf.fill_(-7.0)
+    layer.y_perm.fill_(-7.0)
+    layer.out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    layer.run(stream)
+    torch.cuda.synchronize()
+    assert ffi.fused_error_word(layer.fused_ws) == 0, "a wait between work items timed out"
+    return layer
+
+
+def check_against_oracle(cfg, d, layer, toks=None):
+    idx, w = P.oracle_route(d["logits"], cfg.k)
+    assert np.array_equal(layer.topk_idx.cpu().numpy(), idx)
+    ref = P.oracle_permute(idx, d["src_rank"], cfg, layer.tile_m)
+    real = np.nonzero(ref["row_src"] >= 0)[0]
+    pad = np.setdiff1d(np.arange(layer.perm.R_cap), real)
+    if len(pad):
+        padt = torch.from_numpy(pad).to(layer.out.device)
+        assert torch.all(layer.act_buf[padt] == -7.0) and torch.all(layer.y_perm[padt] == -7.0)
+    if toks is None:
+        toks = list(range(cfg.T))
+        rows = real
+    else:
+        rows = np.unique(ref["inv_perm"][toks][ref["inv_perm"][toks] >= 0])
+    P.check_ffn_rows(cfg, d, ref, layer.act_buf, layer.y_perm, rows, f"fused {cfg.name}")
+    xs = np.zeros((cfg.T, cfg.H))
+    xs[toks] = P.to_np64(d["x"][torch.tensor(toks, device=layer.out.device)])
+    ref_out = O.moe_layer_expert_major(xs, cfg.k, P.host_weights64(d), cfg.act, (idx, w), toks,
+                                       cfg.expert_begin, cfg.n_local)
+    P.assert_output_close(layer.out[torch.tensor(toks, device=layer.out.device)].cpu().double().numpy(), ref_out,
+                          f"fused {cfg.name} out")
+
+
+SMALL = {
+    "swiglu": W.MoEConfig("fs", T=500, H=1536, F=768, E=4, k=2, act="swiglu", logits="normal", tile_m=256),
+    "gelu": W.MoEConfig("fg", T=500, H=1536, F=768, E=4, k=2, act="gelu", logits="normal", tile_m=256),
+    "ranks": W.CONFIGS["ep_share"].with_(T=1200, H=512, F=256),
+}
+
+
+@pytest.mark.parametrize("cus", [0, 32], ids=["all_cus", "one_xcd"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_small_layers_full_check(dev, name, cus):
+    cfg = SMALL[name]
+    d = W.make_inputs(cfg, dev)
+    if cus:
+        h, stream = P.cu_masked_stream(range(cus), dev)
+        try:
+            layer = run_fused(cfg, d, stream)
+        finally:
+            P.destroy_stream(h)
+    else:
+        layer = run_fused(cfg, d)
+    check_against_oracle(cfg, d, layer)
+
+
+def test_fused_repeat_and_graph_replay(dev):
+    # Counters left zero by every launch: repeated launches and replays of a captured launch give the
+    # same bits, with no timed-out wait; the two-call path agrees within fp32 summation order.
+    cfg = SMALL["swiglu"]
+    d = W.make_inputs(cfg, dev)
+    layer = run_fused(cfg, d)
+    first = layer.out.clone()
+    for _ in range(3):
+        layer.out.fill_(0.0)
+        layer.run()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int32), first.view(torch.int32))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.run()
+    for _ in range(3):
+        layer.out.fill_(123.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int32), first.view(torch.int32))
+    assert ffi.fused_error_word(layer.fused_ws) == 0
+    two = MoELayer.from_inputs(cfg, d)
+    two.run()
+    torch.cuda.synchronize()
+    scale = two.out.abs().max().item()
+    err = (two.out - first).abs().max().item()
+    print(f"[parity] fused vs two-call out: max |diff| {err:.3e} (max |out| {scale:.3e})", flush=True)
+    assert err <= 1e-3 * scale
+
+
+@pytest.mark.parametrize("name", ["mixtral", "ep_share", "fine_grained"])
+def test_fused_full_size_sampled(dev, name):
+    cfg = W.CONFIGS[name]
+    d = W.make_inputs(cfg, dev)
+    layer = run_fused(cfg, d)
+    idx, _ = P.oracle_route(d["logits"], cfg.k)
+    toks = P.sample_tokens(cfg.T, 6, idx, cfg.expert_begin, cfg.n_local)
+    check_against_oracle(cfg, d, layer, toks)
+    two = MoELayer.from_inputs(cfg, d)
+    two.run()
+    torch.cuda.synchronize()
+    scale = two.out.abs().max().item()
+    err = (two.out - layer.out).abs().max().item()
+    print(f"[parity] {name}: fused vs two-call out max |diff| {err:.3e} (max |out| {scale:.3e})", flush=True)
+    assert err <= 2e-3 * scale
