@@ -28,7 +28,10 @@
 //              row of each local pair = expert offset + (bucket start - expert
 //              start) + rows of earlier chunks + rank in chunk, written to
 //              row_src / inv_perm, and the token's row copied once from HBM to
-//              each of its rows with the whole row in flight (16-byte loads).
+//              each of its rows with the whole row in flight (16-byte loads,
+//              non-temporal: each token row is read once, and streaming it
+//              cut the placing kernel from 25 to 18 us with cold caches at the
+//              Mixtral shape, warm unchanged).
 //              The blocks also mark the unused rows past the last expert.
 // When hist is too large to copy into every block, a single-block scan (B)
 // writes the (bucket, chunk) prefix and the per-expert outputs between A and
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void permute_place_kernel(
       const intx4* src = x + t * nch;
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (lane + u * kWave < nch) v[u] = src[lane + u * kWave];
+        if (lane + u * kWave < nch) v[u] = __builtin_nontemporal_load(src + lane + u * kWave);
     }
   };
   int64_t tail0;
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(kBlock) void permute_place_kernel(
       if (c0 != lane) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (c0 + u * kWave < nch) v[u] = src[c0 + u * kWave];
+          if (c0 + u * kWave < nch) v[u] = __builtin_nontemporal_load(src + c0 + u * kWave);
       }
       for (int j = 0; j < k; ++j) {
         const int d = __builtin_amdgcn_readlane(p, j);
