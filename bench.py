@@ -403,20 +403,21 @@ def main():
             calls, names = [lay.route, lay.permute, lay.ffn_combine], ["route", "permute", "ffn_combine"]
         else:
             calls, names = [lay.route, lay.permute, lay.ffn, lay.combine], ["route", "permute", "grouped_ffn", "combine"]
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # One event at every call boundary (each record costs the stream a few microseconds, so the end of
+        # one step and the start of the next share one): ev[s * n + i] opens call i of step s, ev[-1] closes
+        # the last step.
+        n = len(calls)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n + 1)]
         torch.cuda.synchronize()
-        start.record(stream)
         for s in range(args.steps):
             for i, c in enumerate(calls):
-                ev[s][i].record(stream)
+                ev[s * n + i].record(stream)
                 c()
-            ev[s][len(calls)].record(stream)
-        end.record(stream)
+        ev[-1].record(stream)
         torch.cuda.synchronize()
-        return (start.elapsed_time(end) / args.steps,
-                {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-                 for i, n in enumerate(names)})
+        return (ev[0].elapsed_time(ev[-1]) / args.steps,
+                {nm: sum(ev[s * n + i].elapsed_time(ev[s * n + i + 1]) for s in range(args.steps)) / args.steps
+                 for i, nm in enumerate(names)})
 
     ms_step, per_call = timed_steps(layer)
 
