@@ -126,7 +126,7 @@ def test_fused_repeat_and_graph_replay(dev):
     assert err <= 1e-3 * scale
 
 
-@pytest.mark.parametrize("name", ["mixtral", "ep_share", "fine_grained"])
+@pytest.mark.parametrize("name", ["mixtral", "ep_share", "fine_grained", "tp2_share", "tp4_share", "tp8_share"])
 def test_fused_full_size_sampled(dev, name):
     cfg = W.CONFIGS[name]
     d = W.make_inputs(cfg, dev)
