@@ -176,23 +176,15 @@ __device__ __forceinline__ void item_coords(int64_t item, int nt, int nbn, int& 
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) { return (bid % kXcds) * (G / kXcds) + bid / kXcds; }
 
-// 8 bytes stored for device-scope visibility: an agent-scope relaxed atomic store, which the
-// compiler emits as a store that writes through this XCD's L2 (sc1), so a workgroup on another XCD that
-// reads the line after the producer's counter increment finds it in memory (its own L2 never held it).
-__device__ __forceinline__ void store8_coh(void* p, uint64_t v) {
-  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Cache-policy bit of a buffer access that makes a store write through this XCD's L2 (sc1), as the
+// compiler emits for an agent-scope atomic store; on a load it is what an agent-scope atomic load uses.
+constexpr int kSc1 = 16;
 
-// Epilogue for 4 consecutive output columns of one row.  COH: the stores are visible device-wide once
-// they have completed (for a consumer in the same launch, see store8_coh).
-template <int EPI, bool COH = false>
+// Epilogue for 4 consecutive output columns of one row.
+template <int EPI>
 __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const float* g, const float* u) {
   static_assert(EPI != EPI_PARTIAL, "partial tiles are stored as two fp32 halves");
-  if (EPI == EPI_F32 && COH) {
-    float* d = static_cast<float*>(C) + row * N + n;
-    store8_coh(d, (uint64_t)__builtin_bit_cast(uint32_t, g[0]) | ((uint64_t)__builtin_bit_cast(uint32_t, g[1]) << 32));
-    store8_coh(d + 2, (uint64_t)__builtin_bit_cast(uint32_t, g[2]) | ((uint64_t)__builtin_bit_cast(uint32_t, g[3]) << 32));
-  } else if (EPI == EPI_F32) {
+  if (EPI == EPI_F32) {
     *reinterpret_cast<floatx4*>(static_cast<float*>(C) + row * N + n) = floatx4{g[0], g[1], g[2], g[3]};
   } else {
     uint16_t h[4];
@@ -201,11 +193,8 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
       const float a = (EPI == EPI_SWIGLU) ? silu_f(g[q]) * u[q] : gelu_f(g[q]);
       h[q] = f2bf_bits(a);
     }
-    const uint2 packed = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-    if (COH)
-      store8_coh(static_cast<uint16_t*>(C) + row * N + n, (uint64_t)packed.x | ((uint64_t)packed.y << 32));
-    else
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) = packed;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + n) =
+        uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
   }
 }
 
@@ -227,6 +216,9 @@ __device__ __forceinline__ void store4(void* C, int64_t row, int N, int n, const
 // GATHER: A is the token matrix x [T, K] itself and padded row p of the tile
 // reads token row_src[p] / topk (row_src < 0: padding, read as zeros) -- the
 // layer0 operand gathered on the fly instead of from a permuted copy.
+//
+// COH: the output is read later in the same launch by workgroups on other
+// XCDs, so it is written through L2, in whole lines (staged through LDS).
 template <int BM, int BN, bool DUAL, int EPI, int STAGES, bool GATHER, bool COH = false>
 __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
@@ -552,6 +544,60 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
 
   // Epilogue: lane holds, for token row m = lane % 32 of each 32-row block,
   // output columns q*8 + (lane/32)*4 + 0..3 (q = 0..3) of each 32-column block.
+  if constexpr (COH) {
+    // Results for consumers on other XCDs are written through L2.  A write-through store that covers
+    // only part of a 128-byte line is completed by a read-modify-write at the memory side, so the tile
+    // is first laid out row-major in LDS (the ring is free once every wave is past its last K step)
+    // and then stored 16 bytes per lane along whole rows: a wavefront covers 1 KiB of one fp32 row
+    // (or four 256-byte bf16 rows) per store, whole lines only.
+    static_assert(!(COH && DUAL && EPI == EPI_PARTIAL), "no split-K pieces of the dual layer here");
+    constexpr int ES = (EPI == EPI_F32 || EPI == EPI_PARTIAL) ? 4 : 2;  // output element bytes
+    constexpr int PITCH = BN * ES + 16;                                 // LDS row pitch (bank offset)
+    constexpr int RING = STAGES * STAGE;
+    constexpr int RP = 256 * PITCH <= RING ? 256 : 128 * PITCH <= RING ? 128 : 64 * PITCH <= RING ? 64 : 32;
+    static_assert(RP * PITCH <= RING && RP % 32 == 0 && (BM % RP) == 0, "staging pass fits the ring");
+    constexpr int CPR = BN * ES / 16;  // 16-byte chunks per output row
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(static_cast<char*>(C) + (c_row0 * ldc + c_n0) * ES, (int64_t)(BM - 1) * ldc * ES + BN * ES);
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int p0 = 0; p0 < BM; p0 += RP) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int mb = wm * WT_M + i * 32;  // first row of this 32-row block
+        if (mb < p0 || mb >= p0 + RP) continue;  // wave-uniform
+        const int ml = mb - p0 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * WT_N + j * 32 + q * 8 + (lane >> 5) * 4;
+            char* d = smem + ml * PITCH + n * ES;
+            if constexpr (ES == 4) {
+              *reinterpret_cast<floatx4*>(d) =
+                  floatx4{acc[0][j][i][q * 4], acc[0][j][i][q * 4 + 1], acc[0][j][i][q * 4 + 2], acc[0][j][i][q * 4 + 3]};
+            } else {
+              uint16_t h[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float g = acc[0][j][i][q * 4 + r], u = acc[NMAT - 1][j][i][q * 4 + r];
+                h[r] = f2bf_bits(EPI == EPI_SWIGLU ? silu_f(g) * u : gelu_f(g));
+              }
+              *reinterpret_cast<uint2*>(d) =
+                  uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+            }
+          }
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < RP * CPR; c += NWAVES * 64) {
+        const int r = c / CPR, cc = c % CPR;
+        if (p0 + r >= valid) break;  // rows are visited in order; the rest of this pass is padding
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * PITCH + cc * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (p0 + r) * ldc * ES + cc * 16, 0, kSc1);
+      }
+      __syncthreads();  // the next pass rewrites the staging rows
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = wm * WT_M + i * 32 + (lane & 31);
@@ -569,12 +615,13 @@ __device__ __forceinline__ void gemm_item(char* smem, const uint16_t* __restrict
           u[r] = acc[NMAT - 1][j][i][q * 4 + r];
         }
         if constexpr (EPI == EPI_PARTIAL) {
-          store4<EPI_F32, COH>(C, row, ldc, n, g, g);
-          if (NMAT == 2) store4<EPI_F32, COH>(C, row, ldc, n + BN, u, u);
+          store4<EPI_F32>(C, row, ldc, n, g, g);
+          if (NMAT == 2) store4<EPI_F32>(C, row, ldc, n + BN, u, u);
         } else {
-          store4<EPI, COH>(C, row, ldc, n, g, u);
+          store4<EPI>(C, row, ldc, n, g, u);
         }
       }
+  }
   }
   wait_vmcnt<0>();  // epilogue stores retired before the next item's load accounting
   __syncthreads();  // the next item's first stages overwrite LDS
@@ -740,7 +787,7 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 // finish returns every counter it used to zero for the next launch.
 // ---------------------------------------------------------------------------
 constexpr int kCombineTokens = 64;
-constexpr int kCombineLoads = 16;   // y rows in flight per thread in a combine item
+constexpr int kCombineWin = 32;     // y rows in flight per thread in a combine item
 constexpr int kMaxTopk = 32;      // the entry point's limit on k
 constexpr int64_t kSpinLimit = 1 << 20;
 
@@ -787,6 +834,8 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(
   __shared__ int s_item, s_flag;
   __shared__ int s_row[kCombineTokens * kMaxTopk];
   __shared__ float s_w[kCombineTokens * kMaxTopk];
+  __shared__ uint8_t s_tok[kCombineTokens * kMaxTopk];
+  __shared__ int s_cnt[kCombineTokens], s_beg[kCombineTokens], s_nslot;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
   int nt = *num_tiles;
@@ -858,21 +907,17 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(
       __syncthreads();
       if (s_flag == S - 1) {  // the last slice of item u: sum the S slices in order, store the rows, signal
         if (ok) {
-          const float* base = part + u * S * (int64_t)(BM * BN1);
+          // 16-byte accesses along whole rows, written through (whole lines, as in the tile epilogue).
+          const __amdgpu_buffer_rsrc_t rp = make_rsrc(part + u * S * (int64_t)(BM * BN1), (int64_t)S * BM * BN1 * 4);
+          const __amdgpu_buffer_rsrc_t ry =
+              make_rsrc(y + (int64_t)row0 * H + nb * BN1, (int64_t)(BM - 1) * H * 4 + BN1 * 4);
           for (int e = threadIdx.x; e < valid * (BN1 / 4); e += 256) {
             const int m = e / (BN1 / 4), c4 = e % (BN1 / 4);
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int q = 0; q < S; ++q) {
-              const float* src = base + q * (int64_t)(BM * BN1) + m * BN1 + c4 * 4;
-              const uint64_t lo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-              const uint64_t hi = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src + 2), __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-              acc += floatx4{__builtin_bit_cast(float, (uint32_t)lo), __builtin_bit_cast(float, (uint32_t)(lo >> 32)),
-                             __builtin_bit_cast(float, (uint32_t)hi), __builtin_bit_cast(float, (uint32_t)(hi >> 32))};
-            }
-            const float g[4] = {acc[0], acc[1], acc[2], acc[3]};
-            store4<EPI_F32, true>(y, (int64_t)row0 + m, H, nb * BN1 + c4 * 4, g, g);
+            for (int q = 0; q < S; ++q)
+              acc += __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rp, (q * (BM * BN1) + m * BN1 + c4 * 4) * 4, 0, kSc1));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ry, (m * H + c4 * 4) * 4, 0, kSc1);
           }
         }
         publish(&group[nb / kGroupN]);
@@ -883,55 +928,77 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(
       const int64_t t0 = (c % TC) * kCombineTokens;
       const int nt_c = (int)(T - t0 < kCombineTokens ? T - t0 : kCombineTokens);
       const int gsize = (nb1 - g * kGroupN) < kGroupN ? (nb1 - g * kGroupN) : kGroupN;
-      // The item's routing slots (row, weight) into LDS while the group's layer1 items finish.
-      for (int e = threadIdx.x; e < nt_c * topk; e += 256) {
-        const int p = inv_perm[t0 * topk + e];
-        s_row[e] = (p < 0 || p >= R_cap) ? -1 : p;
-        s_w[e] = topk_w[t0 * topk + e];
+      // While the group's layer1 items finish: the item's local slots, compacted in token and slot order
+      // (row, weight, token), so that the reads below keep kCombineWin rows in flight whatever the share
+      // of non-local slots.
+      // Thread t < kCombineTokens holds token t0 + t's slots in registers (all its loads in flight at once).
+      const int tt = threadIdx.x;
+      const bool own = tt < nt_c;
+      int pr[kMaxTopk];
+      float pw[kMaxTopk];
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopk; ++j) {
+        pr[j] = -1;
+        pw[j] = 0.f;
+        if (own && j < topk) {
+          const int v = inv_perm[(t0 + tt) * topk + j];
+          pr[j] = (v >= 0 && v < R_cap) ? v : -1;
+          pw[j] = topk_w[(t0 + tt) * topk + j];
+        }
+        n += pr[j] >= 0;
+      }
+      if (tt < kCombineTokens) s_cnt[tt] = n;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int run = 0;
+        for (int t = 0; t < kCombineTokens; ++t) {
+          s_beg[t] = run;
+          run += s_cnt[t];
+        }
+        s_nslot = run;
+      }
+      __syncthreads();
+      if (own) {
+        int o = s_beg[tt];
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j)
+          if (pr[j] >= 0) {
+            s_row[o] = pr[j];
+            s_w[o] = pw[j];
+            s_tok[o] = (uint8_t)tt;
+            ++o;
+          }
       }
       if (threadIdx.x == 0) wait_count(&group[g], nt * gsize, &ctr->err);
       __syncthreads();
       const int col = g * kGroupN * BN1 + threadIdx.x * 4;  // this thread's float4 column of the group
       if (threadIdx.x * 4 < gsize * BN1) {
-        // Up to kCombineLoads rows in flight per thread: U whole tokens at a time (topk above the window:
-        // one token, its first kCombineLoads rows in flight), each token summed in slot order.
-        const int U = topk >= kCombineLoads ? 1 : kCombineLoads / topk;
-        for (int tb = 0; tb < nt_c; tb += U) {
-          const int ue = nt_c - tb < U ? nt_c - tb : U;
-          const int nq = ue * topk;
-          const int* rows = s_row + tb * topk;
-          const float* ws = s_w + tb * topk;
-          floatx4 v[kCombineLoads];
+        for (int t = 0; t < nt_c; ++t)  // tokens with no local slot
+          if (s_cnt[t] == 0) *reinterpret_cast<floatx4*>(out + (t0 + t) * H + col) = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int ns = s_nslot;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < ns; s0 += kCombineWin) {
+          floatx4 v[kCombineWin];
 #pragma unroll
-          for (int q = 0; q < kCombineLoads; ++q) {
-            const int p = q < nq ? rows[q] : -1;
-            v[q] = p >= 0 ? *reinterpret_cast<const floatx4*>(y + (int64_t)p * H + col) : floatx4{0.f, 0.f, 0.f, 0.f};
-          }
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          int j = 0;
-          float* o = out + (t0 + tb) * H + col;
+          for (int q = 0; q < kCombineWin; ++q)
+            v[q] = s0 + q < ns ? *reinterpret_cast<const floatx4*>(y + (int64_t)s_row[s0 + q] * H + col)
+                               : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < kCombineLoads; ++q) {
-            if (q < nq) {
-              acc += ws[q] * v[q];
-              if (++j == topk) {
-                *reinterpret_cast<floatx4*>(o) = acc;
+          for (int q = 0; q < kCombineWin; ++q) {
+            const int sq = s0 + q;
+            if (sq < ns) {
+              acc += s_w[sq] * v[q];  // each token's slots in slot order
+              const int tq = s_tok[sq];
+              if (sq + 1 == ns || s_tok[sq + 1] != tq) {
+                *reinterpret_cast<floatx4*>(out + (t0 + tq) * H + col) = acc;
                 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-                j = 0;
-                o += H;
               }
             }
           }
-          if (topk > kCombineLoads) {
-            for (int q = kCombineLoads; q < topk; ++q) {
-              const int p = rows[q];
-              if (p >= 0) acc += ws[q] * *reinterpret_cast<const floatx4*>(y + (int64_t)p * H + col);
-            }
-            *reinterpret_cast<floatx4*>(o) = acc;
-          }
         }
       }
-      __syncthreads();  // s_row / s_w are rewritten by the next combine item
+      __syncthreads();  // the slot lists are rewritten by the next combine item
     }
   }
   // The last workgroup to finish resets the counters of this launch for the next one.
