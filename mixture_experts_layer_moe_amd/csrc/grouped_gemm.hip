@@ -767,24 +767,27 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
 //
 // Comet section 3.1.2: layer1's N-decomposed reduction can start after its first column blocks;
 // tile-level-signalling follow-up (abstract): tiles are signalled as they become ready instead of
-// waiting for whole kernels.  Here every workgroup takes work items in one global order from a device
-// counter: all layer0 items (256-row tile x 128 columns of F, the unfused order), then layer1 items
-// (tile x 256 columns of H, column groups of kGroupN blocks first), then the K slices of the last
-// layer1 items (as many as the unfused layer1 would leave for its last round), then combine items
-// (64 tokens x one column group, group by group).  Signals:
+// waiting for whole kernels.  Here the work items form one global order: all layer0 items (256-row
+// tile x 128 columns of F, the unfused order), then layer1 items (tile x 256 columns of H, column groups
+// of kGroupN blocks first), then the K slices of the last layer1 items (as many as the unfused layer1
+// would leave for its last round), then combine items (64 tokens x one column group, group by group).
+// Each XCD's workgroups take that order's items from a queue of their own (a device counter per XCD;
+// see the kernel), each queue in increasing order.  Signals:
 //   ready[tile]   layer0 items of the tile done; a layer1 item waits for F / 128 of them;
 //   group[g]      layer1 items (a split item counting once, when its last slice has reduced) of column
 //                 group g done; a combine item waits for num_tiles x (blocks of g) of them;
 //   slices[u]     K slices of split item u done; the one that brings it to S sums all S in slice order.
-// A workgroup only ever waits for items that come before its own in the global order, all of them
-// taken by workgroups that are running, so every wait ends; each is still bounded (on time-out the
-// error word is set and the item proceeds, giving wrong values rather than a hang).
+// Every wait ends: an item only waits for items earlier in the global order, and the earliest item held
+// by a waiting workgroup waits for one that is done, running, or not yet taken from its queue -- and then
+// every workgroup on that queue's XCD holds an earlier item, so none of them waits and the queue moves on
+// (all workgroups are resident: one per CU).  Each wait is still bounded (on time-out the error word is
+// set and the item proceeds, giving wrong values rather than a hang).
 // Visibility across XCDs without an L2 write-back: every result another workgroup reads (activations,
-// layer1 rows, partial slices) is stored with device-scope stores that write through L2; the producer
-// waits for its stores, synchronises its workgroup and then increments the counter; the consumer polls
-// with device-scope loads and then reads the data, which its own L2 and L1 have not held since the
-// launch began (each row range is produced once and read only after its signal).  The last workgroup to
-// finish returns every counter it used to zero for the next launch.
+// layer1 rows, partial slices) is written through L2 in whole lines (gemm_item's COH epilogue); the
+// producer waits for its stores, synchronises its workgroup and then increments the counter; the
+// consumer polls with device-scope loads and then reads the data, which its own L2 and L1 have not held
+// since the launch began (each row range is produced once and read only after its signal).  The last
+// workgroup to finish returns every counter it used to zero for the next launch.
 // ---------------------------------------------------------------------------
 constexpr int kCombineTokens = 64;
 constexpr int kCombineWin = 32;     // y rows in flight per thread in a combine item
@@ -810,7 +813,7 @@ __device__ __forceinline__ bool wait_count(int* p, int target, int* err) {
   }
 }
 
-// After the workgroup's device-scope stores: every wave waits for its own, then thread 0 signals.
+// After the workgroup's write-through stores: every wave waits for its own, then thread 0 signals.
 __device__ __forceinline__ int publish(int* p) {
   wait_vmcnt<0>();
   __syncthreads();
