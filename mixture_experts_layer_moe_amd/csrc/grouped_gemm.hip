@@ -69,10 +69,11 @@
 //   * Epilogue: SwiGLU silu(g) * u, or exact-erf GELU, in fp32, rounded to
 //     bf16 (nearest even) for layer0; plain fp32 for layer1.  Rows past the
 //     expert's real count are never stored.
-//   * Last scheduling round: the items left after the whole rounds run as
-//     half-width pieces, or (with a workspace) as up to 8 K slices whose fp32
-//     partials reduce_slices_kernel sums in order before the layer's
-//     epilogue (layer0's activation included).
+//   * Last scheduling round: the items left after the whole rounds run (with
+//     a workspace) as up to 8 K slices whose fp32 partials
+//     reduce_slices_kernel sums in order before the layer's epilogue
+//     (layer0's activation included), else as half-width pieces when those
+//     fit in one round, else whole.
 //   * Token rows past an expert's real count read as zeros (out-of-range
 //     buffer offsets): they fetch nothing and their MFMAs multiply zeros.
 #include "common.h"
@@ -653,9 +654,11 @@ __host__ __device__ inline int tail_ksplit(int64_t rem, int G, int nk) {
 //    row-major, the up matrix's columns after the gate's);
 //    reduce_slices_kernel sums them in slice order afterwards (and applies
 //    layer0's activation), so the result is deterministic;
-//  * otherwise each is split into two half-width pieces.
-// Either way the last round costs a fraction of a full item instead of
-// leaving most CUs idle behind a few full ones.
+//  * otherwise, if the two half-width pieces of each fit in one round (at
+//    most G / 2 items left), they run as such pieces; else (more than G / 2
+//    items left and no split) the items run whole in one last round.
+// The last round then costs a fraction of a full item instead of leaving
+// most CUs idle behind a few full ones, or at most one full item.
 template <int BM, int BN, bool DUAL, int EPI, int ORDER, int STAGES, bool SPLITK, bool GATHER>
 __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
     const uint16_t* __restrict__ A,    // [R_cap, K] bf16 (x_perm or act)
@@ -705,6 +708,15 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma32_kernel(
       gemm_item<BM, BN, DUAL, EPI_PARTIAL, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0, kb * BK,
                                                            (ke - kb) * BK, ws + piece * (int64_t)PIECE, 0,
                                                            (DUAL ? 2 : 1) * BN, 0, wave, lane, row_src, topk, T);
+    }
+    return;
+  }
+  if (2 * (total - full) > G) {  // the pieces would take two rounds: one round of whole items is shorter
+    for (int64_t item = full + vid; item < total; item += G) {
+      int le, row0, valid, n0;
+      if (!coords(item, le, row0, valid, n0)) continue;
+      gemm_item<BM, BN, DUAL, EPI, STAGES, GATHER>(smem, A, B0, B1, N, K, le, row0, valid, n0, 0, K, C, row0, N, n0,
+                                                   wave, lane, row_src, topk, T);
     }
     return;
   }
