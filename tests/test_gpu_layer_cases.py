@@ -157,6 +157,51 @@ def test_split_k_after_whole_rounds(dev, tile_m, act, fused_gather):
     P.assert_output_close(out.cpu().double().numpy(), ref_out, what + " out")
 
 
+# ---------------------------------------------------------------------------
+# whole rounds, then more than half a grid of items left and no K split: the last round runs whole
+# items (two half-width pieces each would take two rounds); without a workspace the other GEMM's
+# few left-over items run as half-width pieces
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("use_ws", [True, False], ids=["workspace", "no_workspace"])
+def test_whole_last_round(dev, use_ws):
+    # 6 row tiles of 256: layer0 9 column blocks (54 items: 32 whole, 22 left, 22 > 32 / 2 so no
+    # split and no half-width pieces), layer1 6 (36: 32 whole, 4 left: K slices or half-width pieces)
+    cfg = W.MoEConfig("whole", T=500, H=1536, F=1152, E=4, k=2, act="swiglu", logits="normal", tile_m=256)
+    d = W.make_inputs(cfg, dev)
+    idx, w = P.oracle_route(d["logits"], cfg.k)
+    ref = P.oracle_permute(idx, None, cfg, cfg.tile_m)
+    nt = len(ref["tiles"])
+    tcap = ffi.tiles_capacity(cfg.T, cfg.k, cfg.n_local, cfg.tile_m)
+    sched = P.ffn_schedule(nt, tcap, cfg.H, cfg.F, cfg.tile_m, 32)
+    l0 = sched["layer0"]
+    print(f"[schedule] {sched}", flush=True)
+    assert l0["G"] == 32 and l0["full"] > 0 and l0["S"] == 1 and 2 * (l0["total"] - l0["full"]) > l0["G"], l0
+    h, stream = P.cu_masked_stream(range(32), dev)
+    try:
+        layer = MoELayer.from_inputs(cfg, d)
+        layer.route(stream)
+        layer.permute(stream)
+        layer.act_buf.fill_(-7.0)
+        layer.y_perm.fill_(-7.0)
+        torch.cuda.synchronize()
+        ffi.moe_grouped_ffn(layer.perm, layer.w0, layer.w0_up, layer.w1, cfg.act, layer.act_buf, layer.y_perm,
+                            layer.ffn_ws if use_ws else None, stream, use_workspace=use_ws)
+        layer.combine(stream)
+        torch.cuda.synchronize()
+    finally:
+        P.destroy_stream(h)
+    real = np.nonzero(ref["row_src"] >= 0)[0]
+    pad = np.setdiff1d(np.arange(layer.perm.R_cap), real)
+    padt = torch.from_numpy(pad).to(dev)
+    assert torch.all(layer.act_buf[padt] == -7.0) and torch.all(layer.y_perm[padt] == -7.0)
+    what = "whole last round" + (" workspace" if use_ws else " no workspace")
+    P.check_ffn_rows(cfg, d, ref, layer.act_buf, layer.y_perm, real, what)
+    ref_out = O.moe_layer_expert_major(P.to_np64(d["x"]), cfg.k, P.host_weights64(d), cfg.act, (idx, w),
+                                       list(range(cfg.T)))
+    P.assert_output_close(layer.out.cpu().double().numpy(), ref_out, what + " out")
+
+
 def test_layer_on_seven_xcds(dev):
     # The persistent grid follows the stream's CU mask: 224 CUs -> 224 workgroups.  Layer0 then has
     # 224 whole items and 32 left over (7 K slices); layer1 has fewer items than CUs (grid of 80).
