@@ -16,6 +16,11 @@
  *                    rows gathered from x instead of read from x_perm)
  *   moe_combine      top-k weighted reduce back to token order
  *
+ * Two more entry points: moe_ffn_combine_fused runs moe_grouped_ffn and
+ * moe_combine as one persistent launch with tile-level signals, and
+ * moe_permute_noalloc is moe_permute on a fixed per-device scratch array for
+ * callers that cannot allocate.
+ *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise, and
  *     must be 16-byte aligned.  The caller owns all memory: the library never
@@ -32,7 +37,9 @@
  *     without any device-to-host copy.
  *   - bf16 arguments are passed as void* and hold IEEE bfloat16 values.
  *   - Calls are stateless and re-entrant; concurrent calls on different
- *     streams must not share output or workspace buffers.
+ *     streams must not share output or workspace buffers (nor, for
+ *     moe_permute_noalloc, run concurrently on one GPU: they share its
+ *     scratch array).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
