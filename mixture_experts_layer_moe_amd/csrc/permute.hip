@@ -53,7 +53,7 @@ namespace {
 constexpr int kChunk = 256;             // tokens per chunk (one block of kernel A)
 constexpr int kBlock = 1024;            // threads of the place and scan kernels (16 wavefronts)
 constexpr int kWaves = kBlock / kWave;
-constexpr int64_t kFusedReads = 1 << 21;  // place blocks x hist entries up to which hist is copied per block
+constexpr int64_t kFusedReads = 1 << 23;  // place blocks x hist entries up to which hist is copied per block
 
 struct WsLayout {
   int64_t nb, nc;

@@ -159,15 +159,16 @@ def test_permute_many_tiles_with_ranks(dev):
 
 
 def test_permute_large_histogram(dev):
-    # 512 (expert, rank) buckets x 67 chunks of 256 tokens: too many per-chunk counts to copy into every
-    # placing block, so the single-block scan runs between the count and place launches.
-    cfg = W.MoEConfig("m", T=17000, H=64, F=128, E=64, k=4, act="swiglu", logits="normal",
+    # 4096 (expert, rank) buckets x 47 chunks of 256 tokens: too many per-chunk counts to copy into every
+    # placing block (placing blocks x buckets x chunks > 2^23 at every tokens-per-wave choice), so the
+    # single-block scan runs between the count and place launches.
+    cfg = W.MoEConfig("m", T=12000, H=64, F=128, E=512, k=4, act="swiglu", logits="normal",
                       tile_m=32, num_ranks=8)
     d = W.make_inputs(cfg, dev, weights=False)
     idx, _ = P.oracle_route(d["logits"], cfg.k)
-    nb, nc = 64 * 8, (cfg.T + 255) // 256
-    assert nc * nb * nc > 1 << 21
-    check_permute(d["x"], idx, d["src_rank"], cfg.E, 0, 64, 8, 32, dev)
+    nb, nc = 512 * 8, (cfg.T + 255) // 256
+    assert (1 + (cfg.T + 255) // 256) * nb * nc > 1 << 23
+    check_permute(d["x"], idx, d["src_rank"], cfg.E, 0, 512, 8, 32, dev)
 
 
 @pytest.mark.parametrize("case", ["one_token", "all_to_one_expert", "max_buckets", "k_equals_E",
