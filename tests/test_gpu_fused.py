@@ -126,9 +126,14 @@ def test_fused_repeat_and_graph_replay(dev):
     assert err <= 1e-3 * scale
 
 
-@pytest.mark.parametrize("name", ["mixtral", "ep_share", "fine_grained", "tp2_share", "tp4_share", "tp8_share"])
+# A GELU layer with several scheduling rounds of each GEMM (no 256-row GELU workload is in the set).
+GELU_MID = W.MoEConfig("gelu_mid", T=4096, H=2048, F=4096, E=8, k=2, act="gelu", logits="normal", tile_m=256)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "ep_share", "fine_grained", "tp2_share", "tp4_share", "tp8_share",
+                                  "gelu_mid"])
 def test_fused_full_size_sampled(dev, name):
-    cfg = W.CONFIGS[name]
+    cfg = GELU_MID if name == "gelu_mid" else W.CONFIGS[name]
     d = W.make_inputs(cfg, dev)
     layer = run_fused(cfg, d)
     idx, _ = P.oracle_route(d["logits"], cfg.k)
